@@ -1,0 +1,175 @@
+"""Benchmark of the exact-attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one fa_fwd call over one batch of the named workload (inputs already
+resident in HBM). The timed region is K back-to-back calls between two HIP
+events recorded on the stream the kernel is launched on, bracketed by device
+synchronisation. One JSON line is printed. The default workload is the batched
+80x80-map YOLO attention (B=16, H=4, N=6400, d=32, fp16, non-causal); the
+metric also names microseconds per call at N=400, which is measured on the
+20x20-map workload in the same run.
+
+The CPU baseline times the fp64 oracle, unmodified, on a bounded sample of the
+same workload (whole heads, all rows) on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s and % MFMA peak; µs/call at N=400 and N=6400"
+# MI355X dense fp16/bf16 matrix peak: 256 CUs x 4096 FLOP/clk x 2.4 GHz.
+PEAK_MFMA_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_23_amd", "csrc", f)
+                  for f in ("fa_fwd_kernel.hpp", "fa_api.hip")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
+    or None when absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE, encoding="utf-8") as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get("workloads", {}).get(workload)
+    if not ent or ent.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def time_gpu(w, steps: int, warmup: int):
+    import torch
+
+    import exact_attention_23_amd as fa
+    from workloads import make_inputs
+
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in make_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        fa.attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)  # the stream fa_fwd launches on
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        fa.attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    if not torch.isfinite(o.float()).all():
+        raise RuntimeError("non-finite output in the timed run")
+    return ms
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The oracle on whole heads of w until ~budget_s of CPU time is spent."""
+    import numpy as np
+
+    import oracle
+    from workloads import make_inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    q, k, v = make_inputs(w)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    rng = np.random.default_rng(0)
+    order = [heads[i] for i in rng.permutation(len(heads))]
+    done = 0
+    t0 = time.perf_counter()
+    for (b, h) in order:
+        oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                         scale=w.scale, causal=w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = w.flops() * done / len(heads)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads (whole heads, all {w.Nq} query rows) of "
+                      f"{w.name}; {dt:.1f} s wall; numpy float64"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="yolo80b16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-n400", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported. "
+              "The path shards over (batch, head) with no exchange, so per-GPU work is the "
+              "single-GPU kernel at a fraction of the heads.", file=sys.stderr)
+        return 2
+
+    from workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    ms = time_gpu(w, args.steps, args.warmup)
+    tflops = w.flops() / (ms * 1e-3) / 1e12
+    n400_us = None
+    if not args.no_n400 and args.workload != "yolo20":
+        n400_us = time_gpu(WORKLOADS["yolo20"], max(args.steps, 50), args.warmup) * 1e3
+    traffic = measured_traffic(w.name)
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "input_dtype": w.dtype, "accumulate": "fp32",
+                   "parallelism": "single GPU; grid over (batch, head, query block)"},
+        "us_per_call": round(ms * 1e3, 3),
+        "us_per_call_n400": None if n400_us is None else round(n400_us, 3),
+        "mfma_peak_frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": traffic},
+        "algorithmic_hbm_gbs": round(w.algorithmic_bytes() / (ms * 1e-3) / 1e9, 1),
+        "kernel_source_sha": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,54 @@
+"""Compile libfa.so (the HIP kernels and the C ABI) for gfx950, in-tree.
+
+    python -m exact_attention_23_amd.build
+
+hipcc cross-compiles without a GPU present. Every HIP file is built with
+packed-fp32 instructions disabled (-Xclang -target-feature -Xclang
+-packed-fp32-ops); hipcc's host pass warns that it does not know that
+feature, which is harmless.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG_DIR, "csrc")
+LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+ARCH = "gfx950"
+SOURCES = [os.path.join(CSRC, "fa_api.hip")]
+HEADERS = [os.path.join(CSRC, "fa_fwd_kernel.hpp"),
+           os.path.join(os.path.dirname(PKG_DIR), "include", "fa.h")]
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP library cannot be built")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into libfa.so next to this file; return its path."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-o", tmp] + SOURCES
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in r.stdout.splitlines() if noise not in ln]
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
+    sys.exit(0)

@@ -1,0 +1,138 @@
+// fa_api.hip - the C ABI of libfa.so: argument checks, tile selection, grid
+// computation and the launch of the gfx950 attention kernels.
+//
+// The declarations and the contract live in include/fa.h.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_fwd_kernel.hpp"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+typedef void (*KernelFn)(fa::Params);
+
+struct Variant {
+  KernelFn fn;
+  int bm;       // query rows per workgroup
+  int threads;  // threads per workgroup
+};
+
+// Tile shapes per head width: NW waves of 32 query rows, BN keys per tile.
+template <int D, int BN, int NW, typename T>
+Variant make_variant(bool causal) {
+  Variant v;
+  v.fn = causal ? fa::fa_fwd_kernel<D, BN, NW, true, T> : fa::fa_fwd_kernel<D, BN, NW, false, T>;
+  v.bm = 32 * NW;
+  v.threads = 64 * NW;
+  return v;
+}
+
+template <typename T>
+Variant pick(int64_t d, bool causal) {
+  switch (d) {
+    case 32: return make_variant<32, 64, 4, T>(causal);
+    case 64: return make_variant<64, 64, 4, T>(causal);
+    default: return make_variant<128, 64, 4, T>(causal);
+  }
+}
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return kVersion; }
+
+const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULLPTR: return "q, k, v or o is a null pointer";
+    case FA_ERR_SHAPE: return "B, H, Nq and Nk must be >= 1 and Nq*d, Nk*d < 2^31";
+    case FA_ERR_HEADDIM: return "head width d must be 32, 64 or 128";
+    case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16";
+    case FA_ERR_SCALE: return "scale must be finite";
+    case FA_ERR_CAUSAL: return "causal must be 0 or 1";
+    case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case FA_ERR_ALIAS: return "o or lse overlaps an input or each other";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+           float scale, int causal, int dtype, void* stream) {
+  // ---- every check happens before the first HIP call
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_NULLPTR;
+  if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (d != 32 && d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  const int64_t lim = (int64_t)1 << 31;
+  if (Nq * d >= lim || Nk * d >= lim || B > lim || H > lim || B * H >= lim) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
+  if (((uintptr_t)lse) & 3u) return FA_ERR_ALIGN;
+
+  const Variant var = dtype == FA_DTYPE_FP16 ? pick<_Float16>(d, causal != 0)
+                                             : pick<__bf16>(d, causal != 0);
+  const int64_t num_qb = (Nq + var.bm - 1) / var.bm;
+  const int64_t total = B * H * num_qb;
+  if (total >= lim) return FA_ERR_SHAPE;
+
+  const size_t es = 2;
+  const size_t qo_bytes = (size_t)(B * H) * (size_t)(Nq * d) * es;
+  const size_t kv_bytes = (size_t)(B * H) * (size_t)(Nk * d) * es;
+  const size_t lse_bytes = (size_t)(B * H) * (size_t)Nq * 4;
+  if (overlaps(o, qo_bytes, q, qo_bytes) || overlaps(o, qo_bytes, k, kv_bytes) ||
+      overlaps(o, qo_bytes, v, kv_bytes))
+    return FA_ERR_ALIAS;
+  if (lse != nullptr &&
+      (overlaps(lse, lse_bytes, q, qo_bytes) || overlaps(lse, lse_bytes, k, kv_bytes) ||
+       overlaps(lse, lse_bytes, v, kv_bytes) || overlaps(lse, lse_bytes, o, qo_bytes)))
+    return FA_ERR_ALIAS;
+
+  fa::Params p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = (int)B;
+  p.H = (int)H;
+  p.Nq = (int)Nq;
+  p.Nk = (int)Nk;
+  p.num_qb = (int)num_qb;
+  p.total = (int)total;
+  p.xcd_q = (int)(total / 8);
+  p.xcd_r = (int)(total % 8);
+  p.group = 8;
+  if (scale == 0.0f) {  // every logit is 0: zero Q, any positive factor works
+    p.c = 1.0f;
+    p.q_and = 0u;
+    p.q_xor = 0u;
+  } else {  // a negative scale is carried by Q's sign so the factor stays > 0
+    p.c = fabsf(scale) * 1.4426950408889634f;
+    p.q_and = 0xffffffffu;
+    p.q_xor = scale < 0.0f ? 0x80008000u : 0u;
+  }
+
+  void* args[] = {&p};
+  hipError_t e = hipLaunchKernel((const void*)var.fn, dim3((unsigned)total), dim3(var.threads),
+                                 args, 0, (hipStream_t)stream);
+  if (e != hipSuccess) return FA_ERR_LAUNCH;
+  e = hipGetLastError();
+  if (e != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
+}  // extern "C"

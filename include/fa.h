@@ -1,0 +1,100 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) exact-attention forward library, libfa.so.
+ *
+ * Operation (the only one on the path): for every batch b and head h,
+ *
+ *     S   = scale * Q K^T                    (Nq x Nk)
+ *     S_ij = -inf where causal and j > i     (top-left aligned)
+ *     O   = softmax_rows(S) V                (Nq x d)
+ *     LSE_i = ln sum_j exp(S_ij)             (natural log)
+ *
+ * This is the attention formula of "FlashAttention 深度解读" (coreui.cn), section
+ * 背景, and the three-step definition in the kwkr.cn YOLO11 FlashAttention-2
+ * article, section 1.1. The library computes it the way those pages (section 原理
+ * of the former, section 1.2 of the latter) describe: K and V are streamed in
+ * tiles through on-chip memory and each tile updates a running row maximum,
+ * a running exponential sum and a rescaled output accumulator, so the score
+ * matrix S never reaches device memory. Work is spread over (batch, head,
+ * query block), as the kwkr.cn article, section 1.2, says FlashAttention-2
+ * does. The arguments follow scaled_dot_product_attention(q, k, v,
+ * is_causal, scale) as called in that article, section 2.2, with no mask
+ * tensor and no dropout; LSE is the softmax statistic it says training keeps
+ * (section 2.3).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers (HBM of the current HIP device),
+ *     owned and allocated by the caller. The library never allocates, frees
+ *     or synchronises; it enqueues work on `stream` and returns.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream
+ *     of the current device.
+ *   - Every argument is checked before any HIP call is made. A failed check
+ *     returns a positive status and enqueues nothing. There is no fallback to
+ *     another algorithm: an unsupported request is an error.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by fa_fwd. */
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULLPTR = 1, /* q, k, v or o is NULL                                    */
+  FA_ERR_SHAPE = 2,   /* B, H, Nq or Nk < 1, or an index product too large     */
+  FA_ERR_HEADDIM = 3, /* d not in {32, 64, 128}                                 */
+  FA_ERR_DTYPE = 4,   /* dtype not FA_DTYPE_FP16 or FA_DTYPE_BF16               */
+  FA_ERR_SCALE = 5,   /* scale is NaN or infinite                               */
+  FA_ERR_CAUSAL = 6,  /* causal not 0 or 1                                      */
+  FA_ERR_ALIGN = 7,   /* q, k, v, o not 16-byte aligned, or lse not 4-byte      */
+  FA_ERR_ALIAS = 8,   /* o or lse overlaps an input, or o overlaps lse          */
+  FA_ERR_LAUNCH = 9   /* the kernel launch itself failed (hipGetLastError)      */
+};
+
+/* Element types of q, k, v and o (all four share one type). Accumulation is
+ * always fp32. */
+enum fa_dtype { FA_DTYPE_FP16 = 0, FA_DTYPE_BF16 = 1 };
+
+/*
+ * fa_fwd - exact attention forward, O and (optionally) LSE.
+ *
+ *   q      [B, H, Nq, d]  contiguous, row-major, d fastest; dtype elements
+ *   k, v   [B, H, Nk, d]  same layout
+ *   o      [B, H, Nq, d]  output, same layout and dtype; must not overlap
+ *                         q, k, v or lse
+ *   lse    [B, H, Nq]     fp32 output, natural-log log-sum-exp of the scaled,
+ *                         masked scores of each query row; NULL skips it
+ *   B, H   batch and head counts, >= 1
+ *   Nq, Nk query and key/value sequence lengths, >= 1, any value (no multiple
+ *          of 8 or of a tile size is required; the tail is masked). Nq*d and
+ *          Nk*d must stay below 2^31 elements per head.
+ *   d      head width: 32, 64 or 128
+ *   scale  multiplier of Q K^T; any finite value (0 gives uniform weights).
+ *          Callers wanting the usual default pass 1/sqrt(d).
+ *   causal 0: every key is visible; 1: key j is visible to query i iff j <= i
+ *          (top-left alignment, so no row is ever empty)
+ *   dtype  FA_DTYPE_FP16 or FA_DTYPE_BF16
+ *   stream hipStream_t (as void*) the kernel is enqueued on
+ *
+ * Returns FA_OK once the kernel is enqueued, otherwise an fa_status code.
+ * Results are deterministic: the same inputs and arguments give bitwise-equal
+ * outputs (no atomics, fixed reduction order).
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+           float scale, int causal, int dtype, void* stream);
+
+/* A static, human-readable description of a status code (never NULL). */
+const char* fa_status_str(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,121 @@
+"""The C ABI of libfa.so, checked without a GPU.
+
+Every argument check in fa_fwd runs before any HIP call, so invalid calls can
+be made here; no valid (launching) call is made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_23_amd as fa
+from exact_attention_23_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _header_text():
+    with open(HEADER, encoding="utf-8") as f:
+        return f.read()
+
+
+def _declared_functions():
+    src = re.sub(r"/\*.*?\*/", "", _header_text(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = _declared_functions()
+    assert "fa_fwd" in names and "fa_status_str" in names and "fa_version" in names
+    for n in names:
+        assert hasattr(lib, n), f"libfa.so does not export {n}"
+
+
+def test_header_enums_match_binding():
+    src = _header_text()
+    for name in ["FA_OK", "FA_ERR_NULLPTR", "FA_ERR_SHAPE", "FA_ERR_HEADDIM", "FA_ERR_DTYPE",
+                 "FA_ERR_SCALE", "FA_ERR_CAUSAL", "FA_ERR_ALIGN", "FA_ERR_ALIAS", "FA_ERR_LAUNCH",
+                 "FA_DTYPE_FP16", "FA_DTYPE_BF16"]:
+        m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
+        assert m, name
+        assert int(m.group(1)) == getattr(_lib, name), name
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for s in range(0, 10):
+        txt = lib.fa_status_str(s)
+        assert txt and txt.decode() != "unknown status"
+    assert lib.fa_status_str(99).decode() == "unknown status"
+    assert fa.version() >= 100
+
+
+# Fake device addresses: never dereferenced, because each call below fails a
+# check that precedes every HIP call.
+Q, K, V, O, L = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+GOOD = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, Nq=100, Nk=77, d=64, scale=0.125,
+            causal=0, dtype=0, stream=None)
+
+
+def call(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"],
+                     a["d"], a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), _lib.FA_ERR_NULLPTR),
+    (dict(k=0), _lib.FA_ERR_NULLPTR),
+    (dict(v=0), _lib.FA_ERR_NULLPTR),
+    (dict(o=0), _lib.FA_ERR_NULLPTR),
+    (dict(dtype=2), _lib.FA_ERR_DTYPE),
+    (dict(dtype=-1), _lib.FA_ERR_DTYPE),
+    (dict(d=16), _lib.FA_ERR_HEADDIM),
+    (dict(d=96), _lib.FA_ERR_HEADDIM),
+    (dict(d=256), _lib.FA_ERR_HEADDIM),
+    (dict(B=0), _lib.FA_ERR_SHAPE),
+    (dict(H=0), _lib.FA_ERR_SHAPE),
+    (dict(Nq=0), _lib.FA_ERR_SHAPE),
+    (dict(Nk=0), _lib.FA_ERR_SHAPE),
+    (dict(Nq=-5), _lib.FA_ERR_SHAPE),
+    (dict(Nk=(1 << 31) // 64), _lib.FA_ERR_SHAPE),
+    (dict(B=1 << 20, H=1 << 12), _lib.FA_ERR_SHAPE),
+    (dict(causal=2), _lib.FA_ERR_CAUSAL),
+    (dict(causal=-1), _lib.FA_ERR_CAUSAL),
+    (dict(scale=float("nan")), _lib.FA_ERR_SCALE),
+    (dict(scale=float("inf")), _lib.FA_ERR_SCALE),
+    (dict(scale=float("-inf")), _lib.FA_ERR_SCALE),
+    (dict(q=Q + 8), _lib.FA_ERR_ALIGN),
+    (dict(o=O + 2), _lib.FA_ERR_ALIGN),
+    (dict(lse=L + 2), _lib.FA_ERR_ALIGN),
+    (dict(o=Q), _lib.FA_ERR_ALIAS),
+    (dict(o=K + 256), _lib.FA_ERR_ALIAS),
+    (dict(lse=V + 64), _lib.FA_ERR_ALIAS),
+    (dict(lse=O + 1024), _lib.FA_ERR_ALIAS),
+])
+def test_invalid_arguments_rejected_before_launch(kw, status):
+    assert call(**kw) == status
+
+
+def test_check_order_is_stable():
+    # several faults at once: the first check in the documented order wins
+    assert call(q=0, d=3, B=0) == _lib.FA_ERR_NULLPTR
+    assert call(dtype=7, d=3) == _lib.FA_ERR_DTYPE
+    assert call(d=3, B=0) == _lib.FA_ERR_HEADDIM
+
+
+def test_python_wrapper_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa.attention(q, q, q)
+
+
+def test_ctypes_signature():
+    lib = _lib.load()
+    assert lib.fa_fwd.restype is ctypes.c_int
+    assert len(lib.fa_fwd.argtypes) == 14

@@ -1,0 +1,121 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Small shapes are compared element by element over the whole output; they span
+several query blocks and key tiles and end in ragged tails. The five named
+workloads run at their full sizes in the launch configuration the benchmark
+times; there the oracle recomputes sampled rows (each row depends only on its
+query and its head's keys and values).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import compare, default_scale, note, rand_inputs, require_gpu, run_gpu
+from workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+SMALL = [
+    # (B, H, Nq, Nk, d, dtype, causal)
+    (1, 1, 1, 1, 64, "fp16", False),
+    (1, 1, 1, 1, 64, "fp16", True),
+    (1, 2, 2, 2, 32, "fp16", True),
+    (2, 1, 15, 15, 64, "fp16", False),
+    (1, 2, 17, 17, 128, "bf16", True),
+    (1, 1, 31, 33, 32, "bf16", False),
+    (2, 2, 63, 63, 64, "fp16", True),
+    (1, 1, 64, 64, 128, "fp16", False),
+    (1, 3, 65, 65, 32, "fp16", True),
+    (1, 1, 127, 129, 64, "bf16", False),
+    (1, 2, 128, 128, 64, "fp16", True),
+    (2, 1, 129, 129, 128, "bf16", True),
+    (1, 2, 255, 257, 32, "fp16", False),
+    (1, 1, 257, 255, 32, "bf16", True),
+    (3, 2, 361, 361, 64, "fp16", False),
+    (1, 2, 400, 400, 64, "bf16", True),
+    (1, 1, 1000, 1000, 128, "fp16", True),
+    (1, 1, 1000, 1000, 32, "bf16", False),
+    (2, 2, 100, 700, 64, "fp16", False),   # Nq < Nk
+    (1, 2, 700, 100, 64, "fp16", True),    # Nq > Nk, causal
+    (1, 1, 33, 1, 32, "fp16", False),      # one key
+    (1, 1, 1, 513, 128, "bf16", False),    # one query
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%dH%d_q%dk%d_d%d_%s_%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], "causal" if c[6] else "full"))
+def test_small_shapes(case):
+    require_gpu()
+    B, H, Nq, Nk, d, dt, causal = case
+    note(f"parity small {case}")
+    q, k, v = rand_inputs(B, H, Nq, Nk, d, dt, seed=Nq * 1000 + Nk + d)
+    o, lse = run_gpu(q, k, v, causal)
+    O, L = oracle.attention(q, k, v, scale=default_scale(d), causal=causal)
+    compare(o, lse, O, L, what=str(case))
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.5, 1e-3, 2.0])
+def test_scales(scale):
+    require_gpu()
+    note(f"parity scale {scale}")
+    q, k, v = rand_inputs(2, 2, 150, 150, 64, "fp16", seed=77)
+    for causal in (False, True):
+        o, lse = run_gpu(q, k, v, causal, scale=scale)
+        O, L = oracle.attention(q, k, v, scale=scale, causal=causal)
+        compare(o, lse, O, L, what=f"scale={scale} causal={causal}")
+
+
+def test_lse_null():
+    require_gpu()
+    note("parity lse=NULL")
+    q, k, v = rand_inputs(1, 2, 200, 200, 64, "bf16", seed=5)
+    o, lse = run_gpu(q, k, v, True, with_lse=False)
+    assert lse is None
+    O, L = oracle.attention(q, k, v, scale=default_scale(64), causal=True)
+    compare(o, None, O, L, what="lse=NULL")
+
+
+def test_large_logits_tail():
+    """Logits of a few hundred (q, k ~ N(0, 8^2)) over a 19x19 map."""
+    require_gpu()
+    note("parity large logits")
+    for d in (32, 64, 128):
+        q, k, v = rand_inputs(2, 2, 361, 361, d, "fp16", seed=d, sigma_qk=8.0, v_uniform=True)
+        for causal in (False, True):
+            o, lse = run_gpu(q, k, v, causal)
+            O, L = oracle.attention(q, k, v, scale=default_scale(d), causal=causal)
+            compare(o, lse, O, L, what=f"large logits d={d} causal={causal}")
+
+
+SAMPLE_ROWS = 48
+
+
+def _sample_rows(N, rng):
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, 129, 255, 256, N // 2, N - 2, N - 1]
+    rows = set(r for r in fixed if 0 <= r < N)
+    rows.update(int(x) for x in rng.integers(0, N, SAMPLE_ROWS))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", ["yolo20", "yolo80b16", "seq2048", "long16k", "tail361"])
+def test_named_workload_full_size(name):
+    """Each named workload at full size, same call the benchmark times."""
+    require_gpu()
+    w = WORKLOADS[name]
+    note(f"parity workload {name}: B={w.B} H={w.H} N={w.Nq} d={w.d} {w.dtype} causal={w.causal}")
+    q, k, v = make_inputs(w)
+    o, lse = run_gpu(q, k, v, w.causal, scale=w.scale)
+    if w.B * w.H * w.Nq <= 8 * 2 * 400:
+        O, L = oracle.attention(q, k, v, scale=w.scale, causal=w.causal)
+        compare(o, lse, O, L, what=name)
+        return
+    rng = np.random.default_rng(w.seed)
+    heads = sorted(set([(0, 0), (w.B - 1, w.H - 1)] +
+                       [(int(rng.integers(0, w.B)), int(rng.integers(0, w.H))) for _ in range(4)]))
+    for (b, h) in heads:
+        rows = _sample_rows(w.Nq, rng)
+        O, L = oracle.attention_rows(q, k, v, b, h, rows, scale=w.scale, causal=w.causal)
+        compare(o[b, h][rows], lse[b, h][rows], O, L, what=f"{name} head ({b},{h})")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
