@@ -116,6 +116,22 @@ def cpu_baseline(w, budget_s: float = 12.0):
                       f"{w.name}; {dt:.1f} s wall; numpy float64"}
 
 
+def copy_calibration(mib: int, reps: int = 5):
+    """Run a plain device-to-device copy of `mib` MiB `reps` times, so the HBM
+    byte counters can be scaled against a kernel of known traffic."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "reps": reps}),
+          flush=True)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,7 +140,12 @@ def main(argv=None):
     ap.add_argument("--workload", default="yolo80b16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-n400", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain copy kernel of this many MiB (counter scaling)")
     args = ap.parse_args(argv)
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return 0
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported. "
               "The path shards over (batch, head) with no exchange, so per-GPU work is the "

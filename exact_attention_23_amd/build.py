@@ -35,6 +35,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-o", tmp] + SOURCES
     if verbose:
         print(" ".join(cmd), flush=True)

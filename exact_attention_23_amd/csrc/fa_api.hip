@@ -22,12 +22,14 @@ struct Variant {
   int threads;  // threads per workgroup
 };
 
-// Tile shapes per head width: NW waves of 32 query rows, BN keys per tile.
-template <int D, int BN, int NW, typename T>
+// Tile shapes per head width: NW waves of RB 32-row blocks, BN keys per tile,
+// S LDS stages.
+template <int D, int BN, int NW, int RB, int S, typename T>
 Variant make_variant(bool causal) {
   Variant v;
-  v.fn = causal ? fa::fa_fwd_kernel<D, BN, NW, true, T> : fa::fa_fwd_kernel<D, BN, NW, false, T>;
-  v.bm = 32 * NW;
+  v.fn = causal ? fa::fa_fwd_kernel<D, BN, NW, RB, S, true, T>
+                : fa::fa_fwd_kernel<D, BN, NW, RB, S, false, T>;
+  v.bm = 32 * RB * NW;
   v.threads = 64 * NW;
   return v;
 }
@@ -35,9 +37,9 @@ Variant make_variant(bool causal) {
 template <typename T>
 Variant pick(int64_t d, bool causal) {
   switch (d) {
-    case 32: return make_variant<32, 64, 4, T>(causal);
-    case 64: return make_variant<64, 64, 4, T>(causal);
-    default: return make_variant<128, 64, 4, T>(causal);
+    case 32: return make_variant<32, 64, 4, 2, 4, T>(causal);
+    case 64: return make_variant<64, 64, 4, 2, 3, T>(causal);
+    default: return make_variant<128, 64, 8, 1, 4, T>(causal);
   }
 }
 
@@ -56,7 +58,7 @@ const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULLPTR: return "q, k, v or o is a null pointer";
-    case FA_ERR_SHAPE: return "B, H, Nq and Nk must be >= 1 and Nq*d, Nk*d < 2^31";
+    case FA_ERR_SHAPE: return "B, H, Nq and Nk must be >= 1 and Nq*d, Nk*d < 2^29";
     case FA_ERR_HEADDIM: return "head width d must be 32, 64 or 128";
     case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16";
     case FA_ERR_SCALE: return "scale must be finite";
@@ -76,8 +78,12 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (d != 32 && d != 64 && d != 128) return FA_ERR_HEADDIM;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  // Per-head tensors are addressed with 32-bit byte offsets (buffer loads):
+  // keep them below 2^30 bytes so no offset computed in the kernel can wrap.
   const int64_t lim = (int64_t)1 << 31;
-  if (Nq * d >= lim || Nk * d >= lim || B > lim || H > lim || B * H >= lim) return FA_ERR_SHAPE;
+  const int64_t head_lim = (int64_t)1 << 29;
+  if (Nq > head_lim || Nk > head_lim || Nq * d >= head_lim || Nk * d >= head_lim) return FA_ERR_SHAPE;
+  if (B > lim || H > lim || B * H >= lim) return FA_ERR_SHAPE;
   if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
@@ -115,7 +121,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   p.total = (int)total;
   p.xcd_q = (int)(total / 8);
   p.xcd_r = (int)(total % 8);
-  p.group = 8;
+  p.group = 1;
   if (scale == 0.0f) {  // every logit is 0: zero Q, any positive factor works
     p.c = 1.0f;
     p.q_and = 0u;

@@ -10,37 +10,58 @@
 // grows, and adds P V. The score matrix lives only in registers.
 //
 // gfx950 mapping
-//   * A wave owns 32 query rows. Scores are formed transposed, S^T = K Q^T, with
-//     v_mfma_f32_32x32x16_{f16,bf16}: K rows are the A operand (read from
-//     LDS), the wave's Q rows are the B operand and stay in VGPRs for the
-//     whole kernel. In the 32x32 accumulator layout lane l holds column l%32
-//     (its query) and 16 rows (keys), so a query's scores sit in two lanes
-//     (l and l^32) and the row reductions are in-register plus one
-//     cross-lane exchange with the partner lane.
-//   * K rows are written to LDS in a permuted order so that accumulator
+//   * A wave owns RB blocks of 32 query rows. Scores are formed transposed,
+//     S^T = K Q^T, with v_mfma_f32_32x32x16_{f16,bf16}: K rows are the A
+//     operand (16-byte LDS reads), the wave's Q rows are the B operand and stay
+//     in VGPRs for the whole kernel. One K fragment feeds the RB row blocks.
+//     In the 32x32 accumulator layout lane l holds column l%32 (its query) and
+//     16 rows (keys), so a query's scores sit in two lanes (l and l^32) and the
+//     row reductions are in-register plus one exchange with the partner lane.
+//   * K rows are placed in LDS in a permuted order so that accumulator
 //     register i of lane l holds key 16*(l/32)+i of its 32-key subtile. Those
-//     registers, rounded to fp16/bf16, are directly the B operand (P^T) of the
-//     P V product O^T += V^T P^T; V is stored transposed in LDS (Vt[d][key])
-//     so each lane's A operand is one 16-byte LDS read.
+//     registers, rounded to fp16/bf16 in pairs (v_cvt_pk_*), are directly the
+//     B operand (P^T) of O^T += V^T P^T. V stays in its natural [key][d] layout
+//     in LDS and the transposed A operand comes from ds_read_b64_tr_b16, which
+//     hands each lane four consecutive keys of its own d column.
 //   * O^T accumulates in fp32 MFMA accumulators: lane l holds d/2 elements of
 //     its query's output row.
-//   * K/V tiles are fetched with 128-bit global loads into registers one tile
-//     ahead and written into the other half of a double-buffered LDS, so the
-//     fetch of tile j+1 overlaps the math of tile j; one barrier per tile.
-//   * exp is v_exp_f32 (2^x) on scores pre-multiplied by scale*log2(e), folded
-//     into one FMA with the running maximum.
+//   * Global reads are buffer loads whose range is one head's tensor, so rows
+//     and keys past the end read as zero without branches. K/V tiles go from
+//     HBM straight into LDS (buffer_load ... lds, 16 bytes per lane) through a
+//     ring of S stages, S-1 tiles ahead of the math, with no staging
+//     registers; each wave waits on its own loads (vmcnt) and one barrier per
+//     tile publishes a stage to the workgroup. LDS rows are XOR-swizzled in
+//     16-byte chunks against bank conflicts.
+//   * exp is v_exp_f32 (2^x) on scores scaled by scale*log2(e), folded into one
+//     FMA with the running maximum. For fp16 the row sum is accumulated with
+//     v_dot2 from the same rounded P that enters the P V product (the
+//     normalisation then matches the weights actually applied); for bf16 it is
+//     summed in fp32 before rounding, since 8-bit rounding would move the
+//     log-sum-exp by up to 2^-9.
+//   * The running maximum is only raised (and O rescaled) when a tile's maximum
+//     exceeds it by more than 2^8 in the exp2 domain. Until then P stays below
+//     2^8, which fp16/bf16 hold with full relative precision, and the result is
+//     unchanged in exact arithmetic because O and the row sum carry the same
+//     reference maximum.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 struct Params {
   const void* q;
@@ -59,42 +80,97 @@ struct Params {
   uint32_t q_xor; // 0x80008000 flips both halves' sign when scale < 0
 };
 
+// Raising the running maximum is deferred while a tile stays within this many
+// powers of two of it (see the file comment).
+constexpr float kRescaleSlack = 8.0f;
+// Word 3 of a raw buffer resource on gfx9: 32-bit data format, no swizzle.
+constexpr int kBufferFlags = 0x00020000;
+
 template <typename T> struct Mma;
 template <> struct Mma<_Float16> {
   typedef f16x8 vec;
+  typedef f16x2 pair;
   static __device__ __forceinline__ f32x16 run(vec a, vec b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
-    _Float16 a = (_Float16)lo, b = (_Float16)hi;  // round to nearest even
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  // round two floats to nearest-even halves in one v_cvt_pk_f16_f32
+  static __device__ __forceinline__ pair cvt(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    return __builtin_convertvector(f, pair);
+  }
+  // Row sum from the rounded pair (v_dot2 with ones): fp16 keeps 11 bits, so
+  // the sum, and ln of it, move by at most 2^-11 relative.
+  static __device__ __forceinline__ float row_sum(float, float, pair pp, float acc) {
+    const pair one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(pp, one, acc, false);
   }
 };
 template <> struct Mma<__bf16> {
   typedef bf16x8 vec;
+  typedef bf16x2 pair;
   static __device__ __forceinline__ f32x16 run(vec a, vec b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  static __device__ __forceinline__ pair cvt(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    return __builtin_convertvector(f, pair);
+  }
+  // bf16 keeps only 8 bits, so the row sum is taken from the fp32 values to
+  // hold the log-sum-exp to fp32 accuracy.
+  static __device__ __forceinline__ float row_sum(float p0, float p1, pair, float acc) {
+    return acc + (p0 + p1);
   }
 };
 
-// Inverse of the key permutation inside a 32-key subtile: key x = 16*g + i is
-// stored in LDS row 8*(i/4) + 4*g + i%4, which is the accumulator row that
-// register i of a lane in half g covers.
-__device__ __forceinline__ int key_to_lds_row(int x) {
-  return ((x & 15) >> 2) * 8 + (x >> 4) * 4 + (x & 3);
+// Key permutation inside a 32-key subtile: LDS row r holds key
+// 16*((r/4)%2) + 4*(r/8) + r%4, which is the key that accumulator register
+// i = 4*(r/8) + r%4 of a lane in half (r/4)%2 covers.
+__device__ __forceinline__ int lds_row_to_key(int r) {
+  return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3);
 }
 
-// Partner-lane (l ^ 32) combine through ds_bpermute.
+// Byte offset of 16-byte chunk c of row r in a [rows][D] LDS tile: chunks are
+// XOR-swizzled with the row's position inside its 256-byte bank window.
+#ifndef FA_LDS_SWIZZLE
+#define FA_LDS_SWIZZLE 1
+#endif
+template <int D>
+__device__ __forceinline__ int lds_off(int r, int c) {
+  constexpr int kRowsPerWindow = 128 / D;  // rows sharing one 256-byte window
+  constexpr int kChunks = D / 8;
+  const int swz = FA_LDS_SWIZZLE ? (r / kRowsPerWindow) & (kChunks - 1) : 0;
+  return r * (2 * D) + 16 * (c ^ swz);
+}
+
+// One 16-byte-per-lane buffer load straight into LDS: lane l's bytes land at
+// LDS address lds_addr + 16*l. Written as inline asm so that the compiler does
+// not guard every LDS read with a wait for all such loads in flight; the
+// kernel waits for them itself (wait_vmcnt) before the barrier that publishes
+// a stage. M0 is set inside the same asm block; the load has no register
+// result.
+__device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr,
+                                           uint32_t voffset) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(voffset), "s"(rsrc)
+      : "memory", "m0");
+}
+
+// s_waitcnt for vector-memory count <= N only (other counters untouched).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Partner-lane (l ^ 32) exchange through ds_bpermute.
 __device__ __forceinline__ float partner(float x) {
   const int src = ((int)__lane_id() ^ 32) << 2;
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, x)));
 }
-__device__ __forceinline__ float max_with_partner(float x) { return fmaxf(x, partner(x)); }
-__device__ __forceinline__ float sum_with_partner(float x) { return x + partner(x); }
 
 // Workgroup id -> (head, query block). Workgroups are dispatched round-robin
 // over the 8 XCDs; the remap gives each XCD a contiguous range of logical ids
@@ -117,26 +193,27 @@ __device__ __forceinline__ void work_item(const Params& p, int bid, int& head, i
   qb = CAUSAL ? (p.num_qb - 1 - rank) : rank;
 }
 
-template <int D, int BN, int NW, bool CAUSAL, typename T>
+template <int D, int BN, int NW, int RB, int S, bool CAUSAL, typename T>
 __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   using M = Mma<T>;
   using vec = typename M::vec;
-  constexpr int BM = 32 * NW;        // query rows per workgroup
-  constexpr int NT = 64 * NW;        // threads per workgroup
-  constexpr int KS = D / 16;         // k-steps of the QK^T contraction
-  constexpr int NSUB = BN / 32;      // 32-key subtiles per tile
-  constexpr int NDT = D / 32;        // 32-wide d tiles of O
-  constexpr int KSTR = D + 8;        // LDS row stride of K (elements), 16 B pad
-  constexpr int VSTR = BN + 8;       // LDS row stride of V^T (elements), 16 B pad
-  constexpr int KCHUNKS = BN * D / 8;          // 16-byte K chunks per tile
-  constexpr int VUNITS = (BN / 4) * (D / 8);   // 4-key x 8-d V blocks per tile
-  constexpr int KCH = (KCHUNKS + NT - 1) / NT; // per thread (the last may be partial)
-  constexpr int VUN = (VUNITS + NT - 1) / NT;
-  static_assert(KCHUNKS % NT == 0 || KCHUNKS < NT, "K tile must split evenly");
-  static_assert(VUNITS % NT == 0 || VUNITS < NT, "V tile must split evenly");
+  using pair = typename M::pair;
+  constexpr int WR = 32 * RB;          // query rows per wave
+  constexpr int BM = WR * NW;          // query rows per workgroup
+  constexpr int NT = 64 * NW;          // threads per workgroup
+  constexpr int KS = D / 16;           // k-steps of the QK^T contraction
+  constexpr int NSUB = BN / 32;        // 32-key subtiles per tile
+  constexpr int NDT = D / 32;          // 32-wide d tiles of O
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int CHUNKS = BN * CPR;     // chunks per K (or V) tile
+  constexpr int CPT = CHUNKS / NT;     // 16-byte chunks per thread per tensor
+  constexpr int TILE_BYTES = BN * D * 2;
+  constexpr int LOADS = 2 * CPT;       // LDS loads per thread per tile (K and V)
+  static_assert(CPT >= 1 && CPT * NT == CHUNKS, "tile must split evenly over threads");
+  static_assert(BM % BN == 0, "a query block must cover whole key tiles");
+  static_assert(S >= 2 && (S - 2) * LOADS < 64, "stage count out of range");
 
-  __shared__ __attribute__((aligned(16))) T smem_k[2][BN * KSTR];
-  __shared__ __attribute__((aligned(16))) T smem_v[2][D * VSTR];
+  __shared__ __attribute__((aligned(1024))) char smem[S][2][TILE_BYTES];  // [stage][K,V]
 
   int head, qb;
   work_item<CAUSAL>(p, blockIdx.x, head, qb);
@@ -145,25 +222,33 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int half = lane >> 5;  // which 16-key half of a subtile this lane holds
-  const int r32 = lane & 31;   // this lane's query within the wave
+  const int r32 = lane & 31;   // this lane's query within a 32-row block
 
   const int Nq = p.Nq, Nk = p.Nk;
-  const T* __restrict__ Qh = (const T*)p.q + (size_t)head * Nq * D;
-  const T* __restrict__ Kh = (const T*)p.k + (size_t)head * Nk * D;
-  const T* __restrict__ Vh = (const T*)p.v + (size_t)head * Nk * D;
+  const size_t q_head = (size_t)head * Nq * D;
+  const size_t kv_head = (size_t)head * Nk * D;
+  const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const T*)p.q + q_head), (short)0, Nq * D * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const T*)p.k + kv_head), (short)0, Nk * D * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const T*)p.v + kv_head), (short)0, Nk * D * 2, kBufferFlags);
 
-  const int wave_q0 = qb * BM + wave * 32;
-  const int q_row = wave_q0 + r32;
+  const int wave_q0 = qb * BM + wave * WR;
 
-  // ---- this lane's query row as B-operand fragments (8 elements per k-step)
-  vec qf[KS];
+  // ---- this lane's query rows as B-operand fragments (8 elements per k-step)
+  vec qf[RB][KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (q_row < Nq) w = *(const u32x4*)(Qh + (size_t)q_row * D + 16 * s + 8 * half);
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = wave_q0 + 32 * rb + r32;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = (w[e] & p.q_and) ^ p.q_xor;
-    qf[s] = __builtin_bit_cast(vec, w);
+    for (int s = 0; s < KS; ++s) {
+      u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+          q_rsrc, row * (2 * D) + 2 * (16 * s + 8 * half), 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (w[e] & p.q_and) ^ p.q_xor;
+      qf[rb][s] = __builtin_bit_cast(vec, w);
+    }
   }
 
   int kv_end = Nk;
@@ -173,183 +258,249 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   }
   const int ntiles = (kv_end + BN - 1) / BN;
 
-  f32x16 oacc[NDT];
+  f32x16 oacc[RB][NDT];
 #pragma unroll
-  for (int t = 0; t < NDT; ++t)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[t][i] = 0.f;
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[rb][t][i] = 0.f;
+  float m_run[RB], l_run[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = -__builtin_inff();
+    l_run[rb] = 0.f;
+  }
   const float c = p.c;
 
-  // ---- tile fetch (global -> registers) and store (registers -> LDS)
-  u32x4 kreg[KCH];
-  u32x4 vreg[VUN][4];
-  auto fetch = [&](int j) {
-    const int kb = j * BN;
+  // ---- tile loads (HBM -> LDS). Load i of this wave fills the 1 KB block
+  // (wave*CPT + i) of a tile: 16-byte slot sl = 64*block + lane is physical
+  // chunk sl % CPR of tile row sl / CPR, which holds logical chunk
+  // (sl % CPR) ^ swizzle(row). K rows are fetched in the permuted key order,
+  // V rows in natural order.
+  uint32_t k_goff[CPT], v_goff[CPT];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = tid + NT * i;
-      const int row = ch / (D / 8), col = ch % (D / 8);
-      const int key = kb + row;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if ((KCHUNKS >= NT || ch < KCHUNKS) && key < Nk)
-        w = *(const u32x4*)(Kh + (size_t)key * D + col * 8);
-      kreg[i] = w;
-    }
+  for (int i = 0; i < CPT; ++i) {
+    const int sl = (wave * CPT + i) * 64 + lane;
+    const int r = sl / CPR;
+    const int ch = (lds_off<D>(r, sl % CPR) - r * (2 * D)) >> 4;  // logical chunk
+    const int kkey = (r & ~31) | lds_row_to_key(r & 31);
+    k_goff[i] = kkey * (2 * D) + 16 * ch;
+    v_goff[i] = r * (2 * D) + 16 * ch;
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  // Offsets of tiles past the end are pushed beyond every buffer's range:
+  // those loads only write zeros to LDS and touch no memory.
+  constexpr uint32_t kOutOfRange = 0x40000000u;
+  auto issue = [&](int t) {
+    const int st = t % S;
+    const uint32_t gbase = t < ntiles ? (uint32_t)(t * TILE_BYTES) : kOutOfRange;
 #pragma unroll
-    for (int i = 0; i < VUN; ++i) {
-      const int u = tid + NT * i;
-      const int g4 = u % (BN / 4), c8 = u / (BN / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kb + 4 * g4 + r;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if ((VUNITS >= NT || u < VUNITS) && key < Nk)
-          w = *(const u32x4*)(Vh + (size_t)key * D + c8 * 8);
-        vreg[i][r] = w;
-      }
-    }
-  };
-  auto store = [&](int buf) {
-    T* ks = smem_k[buf];
-    T* vs = smem_v[buf];
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = tid + NT * i;
-      if (KCHUNKS < NT && ch >= KCHUNKS) continue;
-      const int row = ch / (D / 8), col = ch % (D / 8);
-      const int lrow = (row & ~31) | key_to_lds_row(row & 31);
-      *(u32x4*)(ks + lrow * KSTR + col * 8) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VUN; ++i) {
-      const int u = tid + NT * i;
-      if (VUNITS < NT && u >= VUNITS) continue;
-      const int g4 = u % (BN / 4), c8 = u / (BN / 4);
-      // transpose 4 keys x 8 d into 8 rows of Vt holding 4 keys each
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
-        const uint32_t a0 = vreg[i][0][w2], a1 = vreg[i][1][w2];
-        const uint32_t a2 = vreg[i][2][w2], a3 = vreg[i][3][w2];
-        u32x2 lo, hi;  // d = 8*c8 + 2*w2 (low halves) and + 1 (high halves)
-        lo[0] = (a0 & 0xffffu) | (a1 << 16);
-        lo[1] = (a2 & 0xffffu) | (a3 << 16);
-        hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-        hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-        const int d0 = 8 * c8 + 2 * w2;
-        *(u32x2*)(vs + d0 * VSTR + 4 * g4) = lo;
-        *(u32x2*)(vs + (d0 + 1) * VSTR + 4 * g4) = hi;
-      }
+    for (int i = 0; i < CPT; ++i) {
+      const uint32_t blk = (uint32_t)((wave * CPT + i) * 1024);
+      dma_to_lds(k_rsrc, __builtin_amdgcn_readfirstlane(lds_base + (2 * st) * TILE_BYTES + blk),
+                 k_goff[i] + gbase);
+      dma_to_lds(v_rsrc, __builtin_amdgcn_readfirstlane(lds_base + (2 * st + 1) * TILE_BYTES + blk),
+                 v_goff[i] + gbase);
     }
   };
 
-  fetch(0);
-  store(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) fetch(j + 1);
-    const int kb = j * BN;
-    // A tile whose first key lies after every row of this wave is fully
-    // masked for it; the wave only helps move data.
-    const bool active = !CAUSAL || kb <= wave_q0 + 31;
-    if (active) {
-      const T* ks = smem_k[buf];
-      const T* vs = smem_v[buf];
-      // ---- S^T = K Q^T for the BN keys of this tile
-      f32x16 sacc[NSUB];
+  // LDS read offsets (bytes) that do not depend on the tile.
+  // K A-operand: row 32t + r32, chunk 2s + half.
+  int k_roff[NSUB][KS];
 #pragma unroll
-      for (int t = 0; t < NSUB; ++t) {
+  for (int t = 0; t < NSUB; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[t][i] = 0.f;
+    for (int s = 0; s < KS; ++s) k_roff[t][s] = lds_off<D>(32 * t + r32, 2 * s + half);
+  // V^T A-operand via transpose reads: lane (group g = lane/16, x = lane%16)
+  // points at key row 32t + 16*half + 8*s2 + 4*jj + x/4 and d columns
+  // 32*dt + 16*(g%2) + 4*(x%4) .. +3; the read returns to lane x the keys
+  // 32t + 16*half + 8*s2 + 4*jj + 0..3 of d column 32*dt + 16*(g%2) + x.
+  const int g16 = (lane >> 4) & 1;
+  const int x16 = lane & 15;
+  int v_roff[NDT][NSUB][2][2];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const vec a = *(const vec*)(ks + (32 * t + r32) * KSTR + 16 * s + 8 * half);
-          sacc[t] = M::run(a, qf[s], sacc[t]);
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int t = 0; t < NSUB; ++t)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int row = 32 * t + 16 * half + 8 * s2 + 4 * jj + (x16 >> 2);
+          const int dcol = 32 * dt + 16 * g16 + 4 * (x16 & 3);
+          v_roff[dt][t][s2][jj] = lds_off<D>(row, dcol >> 3) + 2 * (dcol & 7);
         }
+
+  // One tile of the main loop. MASK selects the instantiation used on the
+  // tiles that need tail or causal masking; the others carry no mask code.
+  auto tile = [&](auto mask_tag, int j) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int st = j % S;
+    const int kb = j * BN;
+    const char* ks = smem[st][0];
+    const char* vs = smem[st][1];
+    // Row block rb sees some key of this tile unless the tile starts after its
+    // last row (causal); such blocks skip the tile entirely.
+    bool act[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) act[rb] = !CAUSAL || kb <= wave_q0 + 32 * rb + 31;
+    if (!act[RB - 1]) return;
+
+    // ---- S^T = K Q^T for the BN keys of this tile
+    f32x16 sacc[RB][NSUB];
+#pragma unroll
+    for (int t = 0; t < NSUB; ++t) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[rb][t][i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const vec a = *(const vec*)(ks + k_roff[t][s]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          if (act[rb]) sacc[rb][t] = M::run(a, qf[rb][s], sacc[rb][t]);
       }
-      // ---- tail / causal masking (only on boundary tiles)
-      const bool tail = kb + BN > Nk;
-      const bool diag = CAUSAL && (kb + BN - 1 > wave_q0);
-      if (tail || diag) {
+      // keep the operand reads of the next subtile from being hoisted here:
+      // they would all be live at once
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- softmax update per row block
+    vec pf[RB][NSUB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (!act[rb]) continue;
+      if (MASK) {
+        // keys kb + 32t + 16*half + i are visible while i < lim - 32t
+        const int q_row = wave_q0 + 32 * rb + r32;
+        int lim = CAUSAL ? (q_row + 1 < Nk ? q_row + 1 : Nk) : Nk;
+        lim -= kb + 16 * half;
 #pragma unroll
         for (int t = 0; t < NSUB; ++t)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb + 32 * t + 16 * half + i;
-            const bool vis = key < Nk && (!CAUSAL || key <= q_row);
-            sacc[t][i] = vis ? sacc[t][i] : -__builtin_inff();
-          }
+          for (int i = 0; i < 16; ++i)
+            sacc[rb][t][i] = (32 * t + i < lim) ? sacc[rb][t][i] : -__builtin_inff();
       }
-      // ---- online softmax update
-      float mx = sacc[0][0];
+      float mx = sacc[rb][0][0];
 #pragma unroll
       for (int t = 0; t < NSUB; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[t][i]);
-      mx = max_with_partner(mx);
-      float m_new = fmaxf(m_run, mx * c);
-      m_new = (m_new == -__builtin_inff()) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      if (__any(m_new > m_run)) {
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[rb][t][i]);
+      mx = fmaxf(mx, partner(mx)) * c;
+      // raise the reference maximum only when the tile exceeds it by more
+      // than the slack (always on the first visible tile: m_run = -inf)
+      if (__any(mx > m_run[rb] + kRescaleSlack)) {
+        float m_new = fmaxf(m_run[rb], mx);
+        m_new = (m_new == -__builtin_inff()) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
 #pragma unroll
         for (int t = 0; t < NDT; ++t)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[t][i] *= alpha;
+          for (int i = 0; i < 16; ++i) oacc[rb][t][i] *= alpha;
+        l_run[rb] *= alpha;
+        m_run[rb] = m_new;
       }
-      l_run *= alpha;
-      m_run = m_new;
-      const float negm = -m_new;
-      vec pf[NSUB][2];
+      const float negm = -m_run[rb];
+      float lsum = l_run[rb];
 #pragma unroll
       for (int t = 0; t < NSUB; ++t) {
         u32x4 w0, w1;
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][i], c, negm));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][i + 1], c, negm));
-          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][i + 8], c, negm));
-          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][i + 9], c, negm));
-          l_run += (p0 + p1) + (p2 + p3);
-          w0[i / 2] = M::pack(p0, p1);
-          w1[i / 2] = M::pack(p2, p3);
+        for (int i = 0; i < 8; ++i) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][t][2 * i], c, negm));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][t][2 * i + 1], c, negm));
+          const pair pp = M::cvt(p0, p1);
+          lsum = M::row_sum(p0, p1, pp, lsum);
+          if (i < 4) w0[i] = __builtin_bit_cast(uint32_t, pp);
+          else w1[i - 4] = __builtin_bit_cast(uint32_t, pp);
         }
-        pf[t][0] = __builtin_bit_cast(vec, w0);
-        pf[t][1] = __builtin_bit_cast(vec, w1);
+        pf[rb][t][0] = __builtin_bit_cast(vec, w0);
+        pf[rb][t][1] = __builtin_bit_cast(vec, w1);
       }
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int t = 0; t < NSUB; ++t)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const vec a = *(const vec*)(vs + (32 * dt + r32) * VSTR + 32 * t + 16 * half + 8 * s2);
-            oacc[dt] = M::run(a, pf[t][s2], oacc[dt]);
-          }
+      l_run[rb] = lsum;
     }
-    if (j + 1 < ntiles) store(buf ^ 1);
+
+    // ---- O^T += V^T P^T
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      if (dt > 0) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < NSUB; ++t)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vs + v_roff[dt][t][s2][0]));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vs + v_roff[dt][t][s2][1]));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          const u32x4 w = {l2[0], l2[1], h2[0], h2[1]};
+          const vec a = __builtin_bit_cast(vec, w);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            if (act[rb]) oacc[rb][dt] = M::run(a, pf[rb][t][s2], oacc[rb][dt]);
+        }
+    }
+  };
+
+  // Tiles from `first_masked` on need masking: the tile holding key Nk-1 when
+  // Nk is not a multiple of BN, and (causal) every tile that reaches past the
+  // first row of the workgroup.
+  int first_masked = (Nk % BN == 0) ? ntiles : Nk / BN;
+  if (CAUSAL) {
+    const int diag = (qb * BM) / BN;  // first tile with a key > row qb*BM
+    first_masked = diag < first_masked ? diag : first_masked;
+  }
+  first_masked = first_masked < ntiles ? first_masked : ntiles;
+
+  // Pipeline: tiles 0..S-2 are requested up front; iteration j requests tile
+  // j+S-1 into the stage tile j-1 used (free since the last barrier), computes
+  // tile j, then waits until at most S-2 tiles of its own loads are pending
+  // (so tile j+1 has landed) and meets the other waves at the barrier.
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t) issue(t);
+  wait_vmcnt<(S - 2) * LOADS>();
+  __syncthreads();
+  // Two loops rather than a per-tile branch, so the accumulators keep one
+  // register assignment through the interior tiles.
+  int j = 0;
+  for (; j < first_masked; ++j) {
+    issue(j + S - 1);
+    tile(std::integral_constant<bool, false>{}, j);
+    wait_vmcnt<(S - 2) * LOADS>();
+    __syncthreads();
+  }
+  for (; j < ntiles; ++j) {
+    issue(j + S - 1);
+    tile(std::integral_constant<bool, true>{}, j);
+    wait_vmcnt<(S - 2) * LOADS>();
     __syncthreads();
   }
 
   // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
-  const float l_tot = sum_with_partner(l_run);
-  const float inv = 1.0f / l_tot;
-  if (q_row < Nq) {
-    T* Oh = (T*)p.o + (size_t)head * Nq * D + (size_t)q_row * D;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+  for (int rb = 0; rb < RB; ++rb) {
+    const int q_row = wave_q0 + 32 * rb + r32;
+    const float l_tot = l_run[rb] + partner(l_run[rb]);
+    const float inv = 1.0f / l_tot;
+    if (q_row < Nq) {
+      T* Oh = (T*)p.o + q_head + (size_t)q_row * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = M::pack(oacc[dt][4 * g + 0] * inv, oacc[dt][4 * g + 1] * inv);
-        w[1] = M::pack(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
-        *(u32x2*)(Oh + 32 * dt + 8 * g + 4 * half) = w;
-      }
-    if (p.lse != nullptr && half == 0)
-      p.lse[(size_t)head * Nq + q_row] = 0.69314718055994531f * (m_run + log2f(l_tot));
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 w;
+          w[0] = __builtin_bit_cast(uint32_t, M::cvt(oacc[rb][dt][4 * g + 0] * inv,
+                                                     oacc[rb][dt][4 * g + 1] * inv));
+          w[1] = __builtin_bit_cast(uint32_t, M::cvt(oacc[rb][dt][4 * g + 2] * inv,
+                                                     oacc[rb][dt][4 * g + 3] * inv));
+          *(u32x2*)(Oh + 32 * dt + 8 * g + 4 * half) = w;
+        }
+      if (p.lse != nullptr && half == 0)
+        p.lse[(size_t)head * Nq + q_row] = 0.69314718055994531f * (m_run[rb] + log2f(l_tot));
+    }
   }
 }
 

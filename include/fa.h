@@ -70,7 +70,8 @@ enum fa_dtype { FA_DTYPE_FP16 = 0, FA_DTYPE_BF16 = 1 };
  *   B, H   batch and head counts, >= 1
  *   Nq, Nk query and key/value sequence lengths, >= 1, any value (no multiple
  *          of 8 or of a tile size is required; the tail is masked). Nq*d and
- *          Nk*d must stay below 2^31 elements per head.
+ *          Nk*d must stay below 2^29 elements per head (1 GiB of fp16), and
+ *          B*H below 2^31.
  *   d      head width: 32, 64 or 128
  *   scale  multiplier of Q K^T; any finite value (0 gives uniform weights).
  *          Callers wanting the usual default pass 1/sqrt(d).

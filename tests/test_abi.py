@@ -82,7 +82,8 @@ def call(**kw):
     (dict(Nq=0), _lib.FA_ERR_SHAPE),
     (dict(Nk=0), _lib.FA_ERR_SHAPE),
     (dict(Nq=-5), _lib.FA_ERR_SHAPE),
-    (dict(Nk=(1 << 31) // 64), _lib.FA_ERR_SHAPE),
+    (dict(Nk=(1 << 29) // 64), _lib.FA_ERR_SHAPE),
+    (dict(Nq=(1 << 29) // 32, d=32), _lib.FA_ERR_SHAPE),
     (dict(B=1 << 20, H=1 << 12), _lib.FA_ERR_SHAPE),
     (dict(causal=2), _lib.FA_ERR_CAUSAL),
     (dict(causal=-1), _lib.FA_ERR_CAUSAL),
