@@ -90,5 +90,8 @@ def attention(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
                     lse.data_ptr() if lse is not None else None,
                     B, H, Nq, Nk, d, scale, 1 if causal else 0, code, stream)
     if st != FA_OK:
-        raise FaError(st, status_str(st))
+        msg = status_str(st)
+        if st == _lib.FA_ERR_LAUNCH:
+            msg += ": " + _lib.load().fa_last_launch_error().decode()
+        raise FaError(st, msg)
     return out, lse

@@ -31,6 +31,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    # PyTorch ships its own HIP runtime under the same soname. Loading torch
+    # first makes libfa.so bind to that copy, so the process has one HIP
+    # runtime; loaded the other way round, torch would bring a second one
+    # that shares no device state with ours.
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # the C ABI checks still work without torch
+        pass
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m exact_attention_23_amd.build` "
@@ -42,6 +50,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd.restype = ctypes.c_int
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_last_launch_error.argtypes = []
+    lib.fa_last_launch_error.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
     lib.fa_version.restype = ctypes.c_int
     _lib = lib

@@ -34,14 +34,29 @@ Variant make_variant(bool causal) {
   return v;
 }
 
+// Tile configuration per head width as (D, BN, NW, RB, S). A build can
+// override them with -DFA_TILES_D32=... etc. to compare configurations.
+#ifndef FA_TILES_D32
+#define FA_TILES_D32 32, 64, 4, 2, 4
+#endif
+#ifndef FA_TILES_D64
+#define FA_TILES_D64 64, 64, 4, 1, 4
+#endif
+#ifndef FA_TILES_D128
+#define FA_TILES_D128 128, 64, 8, 1, 4
+#endif
+
 template <typename T>
 Variant pick(int64_t d, bool causal) {
   switch (d) {
-    case 32: return make_variant<32, 64, 4, 2, 4, T>(causal);
-    case 64: return make_variant<64, 64, 4, 2, 3, T>(causal);
-    default: return make_variant<128, 64, 8, 1, 4, T>(causal);
+    case 32: return make_variant<FA_TILES_D32, T>(causal);
+    case 64: return make_variant<FA_TILES_D64, T>(causal);
+    default: return make_variant<FA_TILES_D128, T>(causal);
   }
 }
+
+// HIP's description of the last failed launch on this thread.
+thread_local const char* g_launch_error = "";
 
 bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
@@ -53,6 +68,8 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 extern "C" {
 
 int fa_version(void) { return kVersion; }
+
+const char* fa_last_launch_error(void) { return g_launch_error; }
 
 const char* fa_status_str(int status) {
   switch (status) {
@@ -135,9 +152,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   void* args[] = {&p};
   hipError_t e = hipLaunchKernel((const void*)var.fn, dim3((unsigned)total), dim3(var.threads),
                                  args, 0, (hipStream_t)stream);
-  if (e != hipSuccess) return FA_ERR_LAUNCH;
-  e = hipGetLastError();
-  if (e != hipSuccess) return FA_ERR_LAUNCH;
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_launch_error = hipGetErrorString(e);
+    return FA_ERR_LAUNCH;
+  }
   return FA_OK;
 }
 

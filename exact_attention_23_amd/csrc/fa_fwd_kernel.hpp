@@ -20,9 +20,12 @@
 //   * K rows are placed in LDS in a permuted order so that accumulator
 //     register i of lane l holds key 16*(l/32)+i of its 32-key subtile. Those
 //     registers, rounded to fp16/bf16 in pairs (v_cvt_pk_*), are directly the
-//     B operand (P^T) of O^T += V^T P^T. V stays in its natural [key][d] layout
-//     in LDS and the transposed A operand comes from ds_read_b64_tr_b16, which
-//     hands each lane four consecutive keys of its own d column.
+//     B operand (P^T) of O^T += V^T P^T. Each V tile is transposed once per
+//     workgroup, one tile ahead, into a V^T buffer: ds_read_b64_tr_b16 hands
+//     each lane four consecutive keys of its own d column, which it stores as
+//     one 8-byte run. The waves then read their V^T operands with 16-byte LDS
+//     reads (the transpose read moves 8 bytes per lane and runs at about a
+//     third of the 16-byte read rate, so it is done once, not once per wave).
 //   * O^T accumulates in fp32 MFMA accumulators: lane l holds d/2 elements of
 //     its query's output row.
 //   * Global reads are buffer loads whose range is one head's tensor, so rows
@@ -49,6 +52,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 namespace fa {
 
@@ -129,17 +133,20 @@ __device__ __forceinline__ int lds_row_to_key(int r) {
   return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3);
 }
 
-// Byte offset of 16-byte chunk c of row r in a [rows][D] LDS tile: chunks are
-// XOR-swizzled with the row's position inside its 256-byte bank window.
-#ifndef FA_LDS_SWIZZLE
-#define FA_LDS_SWIZZLE 1
-#endif
-template <int D>
+// Byte offset of 16-byte chunk c of row r in an LDS tile with ROW_BYTES per
+// row (64, 128 or 256). Chunks are XOR-swizzled per row so that every read
+// pattern of the kernel touches 16 distinct 16-byte bank groups of a
+// 256-byte window per 16 lanes: one chunk of 16 consecutive rows (the MFMA
+// A operands) and 2 adjacent chunks of 4 consecutive rows starting at a
+// multiple of 4 (the transpose reads).
+template <int ROW_BYTES>
 __device__ __forceinline__ int lds_off(int r, int c) {
-  constexpr int kRowsPerWindow = 128 / D;  // rows sharing one 256-byte window
-  constexpr int kChunks = D / 8;
-  const int swz = FA_LDS_SWIZZLE ? (r / kRowsPerWindow) & (kChunks - 1) : 0;
-  return r * (2 * D) + 16 * (c ^ swz);
+  static_assert(ROW_BYTES == 64 || ROW_BYTES == 128 || ROW_BYTES == 256, "row size");
+  int swz;
+  if (ROW_BYTES == 256) swz = ((r & 7) << 1) | ((r >> 3) & 1);             // 1 row per window
+  else if (ROW_BYTES == 128) swz = (((r >> 1) & 3) << 1) | ((r >> 3) & 1);  // 2 rows
+  else swz = (r >> 2) & 3;                                                  // 4 rows
+  return r * ROW_BYTES + 16 * (c ^ swz);
 }
 
 // One 16-byte-per-lane buffer load straight into LDS: lane l's bytes land at
@@ -170,6 +177,24 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ float partner(float x) {
   const int src = ((int)__lane_id() ^ 32) << 2;
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, x)));
+}
+
+// Scheduling-group pattern for a stream of NB operand batches (the first NPV
+// read two 8-byte halves from LDS, the rest one 16-byte row chunk) feeding RB
+// MFMAs each: the reads of the first DEPTH batches, then per batch its MFMAs
+// followed by the reads of the batch DEPTH further on. Masks: DS read 0x100,
+// MFMA 0x8.
+template <int RB, int NPV, int NB, int DEPTH, int B>
+__device__ __forceinline__ void sched_step() {
+  __builtin_amdgcn_sched_group_barrier(0x8, RB, 0);
+  if constexpr (B + DEPTH < NB)
+    __builtin_amdgcn_sched_group_barrier(0x100, (B + DEPTH < NPV) ? 2 : 1, 0);
+}
+template <int RB, int NPV, int NB, int DEPTH, int... Bs>
+__device__ __forceinline__ void sched_pattern(std::integer_sequence<int, Bs...>) {
+  constexpr int kPre = 2 * (DEPTH < NPV ? DEPTH : NPV) + (DEPTH > NPV ? DEPTH - NPV : 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+  (sched_step<RB, NPV, NB, DEPTH, Bs>(), ...);
 }
 
 // Workgroup id -> (head, query block). Workgroups are dispatched round-robin
@@ -209,11 +234,20 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   constexpr int CPT = CHUNKS / NT;     // 16-byte chunks per thread per tensor
   constexpr int TILE_BYTES = BN * D * 2;
   constexpr int LOADS = 2 * CPT;       // LDS loads per thread per tile (K and V)
+  constexpr int TBLK = (BN / 4) * (D / 16);  // 4-key x 16-d blocks of a V tile
+  constexpr int TPW = TBLK / (4 * NW);       // transpose reads per wave per tile
   static_assert(CPT >= 1 && CPT * NT == CHUNKS, "tile must split evenly over threads");
+  static_assert(TPW >= 1 && TPW * 4 * NW == TBLK, "V transpose must split evenly over waves");
   static_assert(BM % BN == 0, "a query block must cover whole key tiles");
-  static_assert(S >= 2 && (S - 2) * LOADS < 64, "stage count out of range");
+  // Loads left in flight at the end of an iteration: the next iteration reads
+  // K of tile j+1 and transposes V of tile j+2, so those must have landed.
+  constexpr int PENDING = (S - 3) * LOADS;
+  static_assert(S >= 3 && PENDING < 64, "stage count out of range");
 
-  __shared__ __attribute__((aligned(1024))) char smem[S][2][TILE_BYTES];  // [stage][K,V]
+  // K and V tiles as loaded ([stage][K,V], rows = keys), and V^T tiles
+  // (rows = d, BN keys each) for the P V operand, double-buffered.
+  __shared__ __attribute__((aligned(1024))) char smem[S][2][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vts[2][TILE_BYTES];
 
   int head, qb;
   work_item<CAUSAL>(p, blockIdx.x, head, qb);
@@ -283,7 +317,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   for (int i = 0; i < CPT; ++i) {
     const int sl = (wave * CPT + i) * 64 + lane;
     const int r = sl / CPR;
-    const int ch = (lds_off<D>(r, sl % CPR) - r * (2 * D)) >> 4;  // logical chunk
+    const int ch = (lds_off<2 * D>(r, sl % CPR) - r * (2 * D)) >> 4;  // logical chunk
     const int kkey = (r & ~31) | lds_row_to_key(r & 31);
     k_goff[i] = kkey * (2 * D) + 16 * ch;
     v_goff[i] = r * (2 * D) + 16 * ch;
@@ -311,67 +345,96 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
 #pragma unroll
   for (int t = 0; t < NSUB; ++t)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) k_roff[t][s] = lds_off<D>(32 * t + r32, 2 * s + half);
-  // V^T A-operand via transpose reads: lane (group g = lane/16, x = lane%16)
-  // points at key row 32t + 16*half + 8*s2 + 4*jj + x/4 and d columns
-  // 32*dt + 16*(g%2) + 4*(x%4) .. +3; the read returns to lane x the keys
-  // 32t + 16*half + 8*s2 + 4*jj + 0..3 of d column 32*dt + 16*(g%2) + x.
-  const int g16 = (lane >> 4) & 1;
-  const int x16 = lane & 15;
-  int v_roff[NDT][NSUB][2][2];
+    for (int s = 0; s < KS; ++s) k_roff[t][s] = lds_off<2 * D>(32 * t + r32, 2 * s + half);
+  // V transpose (once per tile per workgroup): transpose read i of this wave
+  // covers, in 16-lane group g, the block of keys k0..k0+3 and d columns
+  // d0..d0+15 of the V tile; lane x points at key k0 + x/4, columns
+  // d0 + 4*(x%4) .. +3, and receives keys k0..k0+3 of column d0 + x, which it
+  // writes as one 8-byte run into V^T row d0 + x.
+  int tr_src[TPW], tr_dst[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int G = (wave * TPW + i) * 4 + (lane >> 4);
+    const int k0 = 4 * (G % (BN / 4)), d0 = 16 * (G / (BN / 4));
+    const int x = lane & 15;
+    const int col = d0 + 4 * (x & 3);
+    tr_src[i] = lds_off<2 * D>(k0 + (x >> 2), col >> 3) + 2 * (col & 7);
+    tr_dst[i] = lds_off<2 * BN>(d0 + x, k0 >> 3) + 2 * (k0 & 7);
+  }
+  // V^T A-operand: row 32*dt + r32 (a d column), keys 32t + 16*half + 8*s2
+  // .. +7, i.e. chunk 4t + 2*half + s2: one 16-byte read.
+  int v_roff[NDT][NSUB][2];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int t = 0; t < NSUB; ++t)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int row = 32 * t + 16 * half + 8 * s2 + 4 * jj + (x16 >> 2);
-          const int dcol = 32 * dt + 16 * g16 + 4 * (x16 & 3);
-          v_roff[dt][t][s2][jj] = lds_off<D>(row, dcol >> 3) + 2 * (dcol & 7);
-        }
+        v_roff[dt][t][s2] = lds_off<2 * BN>(32 * dt + r32, 4 * t + 2 * half + s2);
 
-  // One tile of the main loop. MASK selects the instantiation used on the
-  // tiles that need tail or causal masking; the others carry no mask code.
-  auto tile = [&](auto mask_tag, int j) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const int st = j % S;
-    const int kb = j * BN;
-    const char* ks = smem[st][0];
-    const char* vs = smem[st][1];
-    // Row block rb sees some key of this tile unless the tile starts after its
-    // last row (causal); such blocks skip the tile entirely.
-    bool act[RB];
+  // V tile j (as loaded) -> V^T buffer j % 2
+  auto transpose_v = [&](int j) {
+    const char* vsrc = smem[j % S][1];
+    char* vdst = vts[j & 1];
+    i16x4 blk[TPW];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) act[rb] = !CAUSAL || kb <= wave_q0 + 32 * rb + 31;
-    if (!act[RB - 1]) return;
+    for (int i = 0; i < TPW; ++i)
+      blk[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vsrc + tr_src[i]));
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) *(i16x4*)(vdst + tr_dst[i]) = blk[i];
+  };
 
-    // ---- S^T = K Q^T for the BN keys of this tile
-    f32x16 sacc[RB][NSUB];
+  // Row block rb sees some key of tile j unless the tile starts after its
+  // last row (causal); such blocks skip the tile.
+  auto active = [&](int j, int rb) { return !CAUSAL || j * BN <= wave_q0 + 32 * rb + 31; };
+
+  // ---- S^T = K Q^T for the BN keys of tile j (K from its LDS stage)
+  auto qk = [&](int j, f32x16 (&sacc)[RB][NSUB]) {
+    const char* ks = smem[j % S][0];
+    const f32x16 zero = {};
+    // k-step outer, subtile inner: consecutive MFMAs feed different accumulators
 #pragma unroll
-    for (int t = 0; t < NSUB; ++t) {
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[rb][t][i] = 0.f;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
+      for (int t = 0; t < NSUB; ++t) {
         const vec a = *(const vec*)(ks + k_roff[t][s]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-          if (act[rb]) sacc[rb][t] = M::run(a, qf[rb][s], sacc[rb][t]);
+          sacc[rb][t] = M::run(a, qf[rb][s], s == 0 ? zero : sacc[rb][t]);
       }
-      // keep the operand reads of the next subtile from being hoisted here:
-      // they would all be live at once
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  };
 
-    // ---- softmax update per row block
-    vec pf[RB][NSUB][2];
+  // P = 2^(S*c - m) for one row block, rounded in pairs into B operands;
+  // returns this tile's contribution to the row sum.
+  auto exp_tile = [&](const f32x16 (&sr)[NSUB], float negm, vec (&pr)[NSUB][2]) {
+    float lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < NSUB; ++t) {
+      u32x4 w0, w1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[t][2 * i], c, negm));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[t][2 * i + 1], c, negm));
+        const pair pp = M::cvt(p0, p1);
+        lsum = M::row_sum(p0, p1, pp, lsum);
+        if (i < 4) w0[i] = __builtin_bit_cast(uint32_t, pp);
+        else w1[i - 4] = __builtin_bit_cast(uint32_t, pp);
+      }
+      pr[t][0] = __builtin_bit_cast(vec, w0);
+      pr[t][1] = __builtin_bit_cast(vec, w1);
+    }
+    return lsum;
+  };
+
+  // ---- online softmax of tile j's scores -> P (fp16/bf16 B operands); O and
+  // the row sums are rescaled when the reference maximum is raised. MASK
+  // selects the instantiation for tiles that need tail or causal masking.
+  auto softmax = [&](auto mask_tag, int j, f32x16 (&sacc)[RB][NSUB], vec (&pf)[RB][NSUB][2]) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int kb = j * BN;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      if (!act[rb]) continue;
+      if (!active(j, rb)) continue;
       if (MASK) {
         // keys kb + 32t + 16*half + i are visible while i < lim - 32t
         const int q_row = wave_q0 + 32 * rb + r32;
@@ -389,8 +452,12 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[rb][t][i]);
       mx = fmaxf(mx, partner(mx)) * c;
-      // raise the reference maximum only when the tile exceeds it by more
-      // than the slack (always on the first visible tile: m_run = -inf)
+      // P against the current reference maximum. Only when the tile exceeds
+      // it by more than the slack (always on the first visible tile, where
+      // m_run = -inf) is the maximum raised, O and l rescaled and P redone;
+      // keeping that rare path out of the common one lets the common path
+      // stay a single block for the scheduler.
+      float lsum = exp_tile(sacc[rb], -m_run[rb], pf[rb]);
       if (__any(mx > m_run[rb] + kRescaleSlack)) {
         float m_new = fmaxf(m_run[rb], mx);
         m_new = (m_new == -__builtin_inff()) ? 0.f : m_new;
@@ -401,48 +468,30 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
           for (int i = 0; i < 16; ++i) oacc[rb][t][i] *= alpha;
         l_run[rb] *= alpha;
         m_run[rb] = m_new;
+        lsum = exp_tile(sacc[rb], -m_new, pf[rb]);
       }
-      const float negm = -m_run[rb];
-      float lsum = l_run[rb];
-#pragma unroll
-      for (int t = 0; t < NSUB; ++t) {
-        u32x4 w0, w1;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][t][2 * i], c, negm));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][t][2 * i + 1], c, negm));
-          const pair pp = M::cvt(p0, p1);
-          lsum = M::row_sum(p0, p1, pp, lsum);
-          if (i < 4) w0[i] = __builtin_bit_cast(uint32_t, pp);
-          else w1[i - 4] = __builtin_bit_cast(uint32_t, pp);
-        }
-        pf[rb][t][0] = __builtin_bit_cast(vec, w0);
-        pf[rb][t][1] = __builtin_bit_cast(vec, w1);
-      }
-      l_run[rb] = lsum;
+      l_run[rb] += lsum;
     }
+  };
 
-    // ---- O^T += V^T P^T
-    __builtin_amdgcn_sched_barrier(0);
+  // ---- O^T += V^T P^T for tile j (V^T from its transposed buffer)
+  auto pv = [&](int j, vec (&pf)[RB][NSUB][2]) {
+    const char* vs = vts[j & 1];
+    bool act[RB];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      if (dt > 0) __builtin_amdgcn_sched_barrier(0);
+    for (int rb = 0; rb < RB; ++rb) act[rb] = active(j, rb);
+    // key chunk outer, d tile inner: consecutive MFMAs feed different accumulators
 #pragma unroll
-      for (int t = 0; t < NSUB; ++t)
+    for (int t = 0; t < NSUB; ++t)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vs + v_roff[dt][t][s2][0]));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vs + v_roff[dt][t][s2][1]));
-          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-          const u32x4 w = {l2[0], l2[1], h2[0], h2[1]};
-          const vec a = __builtin_bit_cast(vec, w);
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const vec a = *(const vec*)(vs + v_roff[dt][t][s2]);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             if (act[rb]) oacc[rb][dt] = M::run(a, pf[rb][t][s2], oacc[rb][dt]);
         }
-    }
   };
 
   // Tiles from `first_masked` on need masking: the tile holding key Nk-1 when
@@ -455,29 +504,35 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   }
   first_masked = first_masked < ntiles ? first_masked : ntiles;
 
-  // Pipeline: tiles 0..S-2 are requested up front; iteration j requests tile
-  // j+S-1 into the stage tile j-1 used (free since the last barrier), computes
-  // tile j, then waits until at most S-2 tiles of its own loads are pending
-  // (so tile j+1 has landed) and meets the other waves at the barrier.
+  // Pipeline. Tiles 0..S-2 are requested up front; iteration j requests tile
+  // j+S-1 into the stage of tile j-1 (free since the last barrier), writes
+  // V^T of tile j+1 (its stage has landed), runs QK^T, softmax and P V of
+  // tile j (V^T of tile j was written before the last barrier), then waits
+  // until tile j+2 has landed (its own loads) and meets the other waves at the
+  // barrier. Past the last tile the stages hold zeros from out-of-range loads.
 #pragma unroll
   for (int t = 0; t < S - 1; ++t) issue(t);
-  wait_vmcnt<(S - 2) * LOADS>();
+  wait_vmcnt<PENDING>();
   __syncthreads();
+  transpose_v(0);
+  __syncthreads();
+  vec pf[RB][NSUB][2];
+  f32x16 sc[RB][NSUB];
+  auto step = [&](auto mask_tag, int j) {
+    issue(j + S - 1);
+    transpose_v(j + 1);
+    qk(j, sc);
+    __builtin_amdgcn_sched_barrier(0);
+    softmax(mask_tag, j, sc, pf);
+    pv(j, pf);
+    wait_vmcnt<PENDING>();
+    __syncthreads();
+  };
   // Two loops rather than a per-tile branch, so the accumulators keep one
   // register assignment through the interior tiles.
   int j = 0;
-  for (; j < first_masked; ++j) {
-    issue(j + S - 1);
-    tile(std::integral_constant<bool, false>{}, j);
-    wait_vmcnt<(S - 2) * LOADS>();
-    __syncthreads();
-  }
-  for (; j < ntiles; ++j) {
-    issue(j + S - 1);
-    tile(std::integral_constant<bool, true>{}, j);
-    wait_vmcnt<(S - 2) * LOADS>();
-    __syncthreads();
-  }
+  for (; j < first_masked; ++j) step(std::integral_constant<bool, false>{}, j);
+  for (; j < ntiles; ++j) step(std::integral_constant<bool, true>{}, j);
 
   // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
 #pragma unroll

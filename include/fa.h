@@ -91,6 +91,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /* A static, human-readable description of a status code (never NULL). */
 const char* fa_status_str(int status);
 
+/* HIP's description of the error behind the calling thread's last
+ * FA_ERR_LAUNCH (static string, "" if none). */
+const char* fa_last_launch_error(void);
+
 /* Library version as major*10000 + minor*100 + patch. */
 int fa_version(void);
 
