@@ -132,6 +132,60 @@ def copy_calibration(mib: int, reps: int = 5):
           flush=True)
 
 
+def _counter_rows(csv_dir: str, counter: str):
+    """(kernel name, value) rows of one rocprofv3 --pmc CSV output directory."""
+    import csv
+    import glob
+
+    rows = []
+    for f in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def write_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str,
+                  copy_write_dir: str, copy_mib: int, command: str):
+    """Record HBM bytes per launch of the attention kernel from rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch), each scaled by what the
+    same counter reads for a plain copy of copy_mib MiB (known bytes)."""
+    import statistics
+
+    known = copy_mib * (1 << 20)
+    cf = [v for k, v in _counter_rows(copy_fetch_dir, "FETCH_SIZE") if "copyBuffer" in k or "copy" in k.lower()]
+    cw = [v for k, v in _counter_rows(copy_write_dir, "WRITE_SIZE") if "copyBuffer" in k or "copy" in k.lower()]
+    kf = [v for k, v in _counter_rows(fetch_dir, "FETCH_SIZE") if "fa_fwd_kernel" in k]
+    kw = [v for k, v in _counter_rows(write_dir, "WRITE_SIZE") if "fa_fwd_kernel" in k]
+    if not (cf and cw and kf and kw):
+        raise RuntimeError("missing counter rows")
+    f_scale = known / (statistics.median(cf) * 1024)
+    w_scale = known / (statistics.median(cw) * 1024)
+    fetch = statistics.median(kf) * 1024 * f_scale
+    write = statistics.median(kw) * 1024 * w_scale
+    try:
+        with open(TRAFFIC_FILE, encoding="utf-8") as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        rec = {}
+    rec.setdefault("about", "HBM bytes per launch of fa_fwd_kernel from rocprofv3 FETCH_SIZE and "
+                   "WRITE_SIZE (KiB per dispatch), scaled by the same counters on a plain "
+                   "device copy of known size. Written by bench.py --write-traffic.")
+    rec.setdefault("workloads", {})[workload] = {
+        "kernel_source_sha": kernel_source_hash(),
+        "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
+        "hbm_bytes_per_launch": round(fetch + write),
+        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+        "copy_calibration_mib": copy_mib, "command": command,
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w", encoding="utf-8") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    return rec["workloads"][workload]
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,7 +196,15 @@ def main(argv=None):
     ap.add_argument("--no-n400", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain copy kernel of this many MiB (counter scaling)")
+    ap.add_argument("--write-traffic", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                         "COPY_WRITE_DIR", "COPY_MIB"),
+                    help="record HBM traffic of --workload from rocprofv3 --pmc CSV directories")
+    ap.add_argument("--command", default="", help="profiling command recorded with --write-traffic")
     args = ap.parse_args(argv)
+    if args.write_traffic:
+        fd, wd, cfd, cwd, mib = args.write_traffic
+        print(json.dumps(write_traffic(args.workload, fd, wd, cfd, cwd, int(mib), args.command)))
+        return 0
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
         return 0
