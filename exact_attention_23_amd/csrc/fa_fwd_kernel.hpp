@@ -36,9 +36,10 @@
 //     tile publishes a stage to the workgroup. LDS rows are XOR-swizzled in
 //     16-byte chunks against bank conflicts.
 //   * exp is v_exp_f32 (2^x) on scores scaled by scale*log2(e), folded into one
-//     FMA with the running maximum. For fp16 the row sum is accumulated with
-//     v_dot2 from the same rounded P that enters the P V product (the
-//     normalisation then matches the weights actually applied); for bf16 it is
+//     FMA with the running maximum. For fp16 the row sum is accumulated on the
+//     matrix cores (a 16x16x32 MFMA against a 0/1 selector) from the same
+//     rounded P that enters the P V product, so the normalisation matches the
+//     weights actually applied and the vector units are spared; for bf16 it is
 //     summed in fp32 before rounding, since 8-bit rounding would move the
 //     log-sum-exp by up to 2^-9.
 //   * The running maximum is only raised (and O rescaled) when a tile's maximum
@@ -62,6 +63,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -102,12 +104,11 @@ template <> struct Mma<_Float16> {
     f32x2 f = {lo, hi};
     return __builtin_convertvector(f, pair);
   }
-  // Row sum from the rounded pair (v_dot2 with ones): fp16 keeps 11 bits, so
-  // the sum, and ln of it, move by at most 2^-11 relative.
-  static __device__ __forceinline__ float row_sum(float, float, pair pp, float acc) {
-    const pair one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(pp, one, acc, false);
-  }
+  // The row sum is taken on the matrix cores from the same rounded P that
+  // enters P V (see row_sum_mfma); fp16 keeps 11 bits, so the sum, and ln of
+  // it, move by at most 2^-11 relative.
+  static constexpr bool kMfmaRowSum = true;
+  static __device__ __forceinline__ float row_sum(float, float, pair, float acc) { return acc; }
 };
 template <> struct Mma<__bf16> {
   typedef bf16x8 vec;
@@ -121,6 +122,7 @@ template <> struct Mma<__bf16> {
   }
   // bf16 keeps only 8 bits, so the row sum is taken from the fp32 values to
   // hold the log-sum-exp to fp32 accuracy.
+  static constexpr bool kMfmaRowSum = false;
   static __device__ __forceinline__ float row_sum(float p0, float p1, pair, float acc) {
     return acc + (p0 + p1);
   }
@@ -173,10 +175,24 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Partner-lane (l ^ 32) exchange through ds_bpermute.
-__device__ __forceinline__ float partner(float x) {
-  const int src = ((int)__lane_id() ^ 32) << 2;
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, x)));
+// Combine a value with the partner lane's (l ^ 32) through v_permlane32_swap,
+// which swaps the upper 32 lanes of its first operand with the lower 32 lanes
+// of its second: with both holding x, every lane ends up with x and x[l ^ 32]
+// in the two registers. (Written as inline asm because the compiler builtin
+// for this instruction drops its second result.) The s_nop pairs give the
+// wait states around the cross-lane move.
+__device__ __forceinline__ void swap_with_partner(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float max_with_partner(float x) {
+  float a = x, b = x;
+  swap_with_partner(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_with_partner(float x) {
+  float a = x, b = x;
+  swap_with_partner(a, b);
+  return a + b;
 }
 
 // Scheduling-group pattern for a stream of NB operand batches (the first NPV
@@ -254,7 +270,10 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // Wave index in a scalar register: every per-wave condition below (which
+  // row blocks see a tile) must compile to a scalar branch, never to an
+  // EXEC mask, because MFMA instructions ignore EXEC.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;  // which 16-key half of a subtile this lane holds
   const int r32 = lane & 31;   // this lane's query within a 32-row block
 
@@ -300,11 +319,24 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[rb][t][i] = 0.f;
   float m_run[RB], l_run[RB];
+  // fp16 row sums, accumulated by MFMA (every register of a lane holds the
+  // sum for the lane's own query)
+  f32x4 lacc[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m_run[rb] = -__builtin_inff();
     l_run[rb] = 0.f;
+    lacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // A operand of the row-sum MFMA (16x16x32): lane l holds row l%16 of the
+  // 16x32 selector, for k group l/16. Row m picks the k groups of its own
+  // query: A[m][k] = 1 iff (m/4)%2 == (k/8)%2. With B = the P operand (lane l
+  // supplies k group l/16 of column l%16, i.e. 8 keys of query l%32), output
+  // row m of column n sums the 16 keys of query n + 16*((m/4)%2), and the
+  // 16x16 output layout puts rows 4*(l/16)..+3 of column l%16 in lane l: the
+  // lane's own query l%32.
+  const _Float16 sel_h = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? (_Float16)1.0f : (_Float16)0.0f;
+  const f16x8 row_sel = {sel_h, sel_h, sel_h, sel_h, sel_h, sel_h, sel_h, sel_h};
   const float c = p.c;
 
   // ---- tile loads (HBM -> LDS). Load i of this wave fills the 1 KB block
@@ -446,12 +478,15 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
           for (int i = 0; i < 16; ++i)
             sacc[rb][t][i] = (32 * t + i < lim) ? sacc[rb][t][i] : -__builtin_inff();
       }
-      float mx = sacc[rb][0][0];
+      // row maximum: four independent chains, then the partner lane
+      float m4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m4[k] = sacc[rb][0][k];
 #pragma unroll
       for (int t = 0; t < NSUB; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[rb][t][i]);
-      mx = fmaxf(mx, partner(mx)) * c;
+        for (int i = (t == 0 ? 4 : 0); i < 16; ++i) m4[i & 3] = fmaxf(m4[i & 3], sacc[rb][t][i]);
+      const float mx = max_with_partner(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * c;
       // P against the current reference maximum. Only when the tile exceeds
       // it by more than the slack (always on the first visible tile, where
       // m_run = -inf) is the maximum raised, O and l rescaled and P redone;
@@ -467,6 +502,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[rb][t][i] *= alpha;
         l_run[rb] *= alpha;
+        if constexpr (M::kMfmaRowSum) lacc[rb] *= alpha;
         m_run[rb] = m_new;
         lsum = exp_tile(sacc[rb], -m_new, pf[rb]);
       }
@@ -491,6 +527,15 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             if (act[rb]) oacc[rb][dt] = M::run(a, pf[rb][t][s2], oacc[rb][dt]);
+          if constexpr (M::kMfmaRowSum) {
+            if (dt == 0) {
+#pragma unroll
+              for (int rb = 0; rb < RB; ++rb)
+                if (act[rb])
+                  lacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                      row_sel, __builtin_bit_cast(f16x8, pf[rb][t][s2]), lacc[rb], 0, 0, 0);
+            }
+          }
         }
   };
 
@@ -538,7 +583,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int q_row = wave_q0 + 32 * rb + r32;
-    const float l_tot = l_run[rb] + partner(l_run[rb]);
+    const float l_tot = M::kMfmaRowSum ? lacc[rb][0] : sum_with_partner(l_run[rb]);
     const float inv = 1.0f / l_tot;
     if (q_row < Nq) {
       T* Oh = (T*)p.o + q_head + (size_t)q_row * D;
