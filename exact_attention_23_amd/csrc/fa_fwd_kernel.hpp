@@ -36,17 +36,20 @@
 //     tile publishes a stage to the workgroup. LDS rows are XOR-swizzled in
 //     16-byte chunks against bank conflicts.
 //   * exp is v_exp_f32 (2^x) on scores scaled by scale*log2(e), folded into one
-//     FMA with the running maximum. For fp16 the row sum is accumulated on the
+//     FMA with the reference maximum. For fp16 the row sum is taken on the
 //     matrix cores (a 16x16x32 MFMA against a 0/1 selector) from the same
 //     rounded P that enters the P V product, so the normalisation matches the
 //     weights actually applied and the vector units are spared; for bf16 it is
 //     summed in fp32 before rounding, since 8-bit rounding would move the
 //     log-sum-exp by up to 2^-9.
-//   * The running maximum is only raised (and O rescaled) when a tile's maximum
-//     exceeds it by more than 2^8 in the exp2 domain. Until then P stays below
-//     2^8, which fp16/bf16 hold with full relative precision, and the result is
-//     unchanged in exact arithmetic because O and the row sum carry the same
-//     reference maximum.
+//   * The reference maximum lags the true running maximum: P of a tile is
+//     formed against it first, and only when that tile's row sum exceeds 2^15
+//     (or is not finite, as on a row's first tile) is the maximum of the tile
+//     taken, O and the row sum rescaled and P redone. The row sum bounds every
+//     P of the row, so P always stays finite in fp16 and keeps full relative
+//     precision; the result is unchanged in exact arithmetic because O and the
+//     row sum carry the same reference. The common path thus needs no row
+//     maximum at all: per score it is one FMA, one exp2 and half a conversion.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -86,9 +89,10 @@ struct Params {
   uint32_t q_xor; // 0x80008000 flips both halves' sign when scale < 0
 };
 
-// Raising the running maximum is deferred while a tile stays within this many
-// powers of two of it (see the file comment).
-constexpr float kRescaleSlack = 8.0f;
+// Largest tile row sum, relative to the reference maximum, that is accepted
+// without raising the maximum (see the file comment). Every P of the tile is
+// at most its row sum, so each stays below 2^15 and is finite in fp16.
+constexpr float kTileSumLimit = 32768.0f;
 // Word 3 of a raw buffer resource on gfx9: 32-bit data format, no swizzle.
 constexpr int kBufferFlags = 0x00020000;
 
@@ -184,33 +188,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void swap_with_partner(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
 }
+// IEEE maximum (v_maximum*_f32): unlike fmaxf it needs no canonicalising of
+// its operands. Scores are never NaN for finite inputs.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float max_with_partner(float x) {
   float a = x, b = x;
   swap_with_partner(a, b);
-  return fmaxf(a, b);
+  return vmax(a, b);
 }
 __device__ __forceinline__ float sum_with_partner(float x) {
   float a = x, b = x;
   swap_with_partner(a, b);
   return a + b;
-}
-
-// Scheduling-group pattern for a stream of NB operand batches (the first NPV
-// read two 8-byte halves from LDS, the rest one 16-byte row chunk) feeding RB
-// MFMAs each: the reads of the first DEPTH batches, then per batch its MFMAs
-// followed by the reads of the batch DEPTH further on. Masks: DS read 0x100,
-// MFMA 0x8.
-template <int RB, int NPV, int NB, int DEPTH, int B>
-__device__ __forceinline__ void sched_step() {
-  __builtin_amdgcn_sched_group_barrier(0x8, RB, 0);
-  if constexpr (B + DEPTH < NB)
-    __builtin_amdgcn_sched_group_barrier(0x100, (B + DEPTH < NPV) ? 2 : 1, 0);
-}
-template <int RB, int NPV, int NB, int DEPTH, int... Bs>
-__device__ __forceinline__ void sched_pattern(std::integer_sequence<int, Bs...>) {
-  constexpr int kPre = 2 * (DEPTH < NPV ? DEPTH : NPV) + (DEPTH > NPV ? DEPTH - NPV : 0);
-  __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
-  (sched_step<RB, NPV, NB, DEPTH, Bs>(), ...);
 }
 
 // Workgroup id -> (head, query block). Workgroups are dispatched round-robin
@@ -318,17 +307,16 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
     for (int t = 0; t < NDT; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[rb][t][i] = 0.f;
+  // Running reference maximum (exp2 domain) and row sum relative to it. For
+  // fp16 l_run is the whole row's sum; for bf16 it covers the lane's half of
+  // the keys and is combined with the partner lane at the end.
   float m_run[RB], l_run[RB];
-  // fp16 row sums, accumulated by MFMA (every register of a lane holds the
-  // sum for the lane's own query)
-  f32x4 lacc[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m_run[rb] = -__builtin_inff();
     l_run[rb] = 0.f;
-    lacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // A operand of the row-sum MFMA (16x16x32): lane l holds row l%16 of the
+  // A operand of the fp16 row-sum MFMA (16x16x32): lane l holds row l%16 of the
   // 16x32 selector, for k group l/16. Row m picks the k groups of its own
   // query: A[m][k] = 1 iff (m/4)%2 == (k/8)%2. With B = the P operand (lane l
   // supplies k group l/16 of column l%16, i.e. 8 keys of query l%32), output
@@ -458,8 +446,26 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
     return lsum;
   };
 
+  // Row sum of a tile's P: for fp16, four 16x16x32 MFMAs of the selector
+  // against the rounded P (each lane gets its own query's sum); for bf16 the
+  // fp32 partial sum exp_tile returned.
+  auto tile_sum = [&](float lsum, const vec (&pr)[NSUB][2]) -> float {
+    if constexpr (M::kMfmaRowSum) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < NSUB; ++t)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(row_sel, __builtin_bit_cast(f16x8, pr[t][s2]),
+                                                       acc, 0, 0, 0);
+      return acc[0];
+    } else {
+      return lsum;
+    }
+  };
+
   // ---- online softmax of tile j's scores -> P (fp16/bf16 B operands); O and
-  // the row sums are rescaled when the reference maximum is raised. MASK
+  // the row sum are rescaled when the reference maximum is raised. MASK
   // selects the instantiation for tiles that need tail or causal masking.
   auto softmax = [&](auto mask_tag, int j, f32x16 (&sacc)[RB][NSUB], vec (&pf)[RB][NSUB][2]) {
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -478,23 +484,25 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
           for (int i = 0; i < 16; ++i)
             sacc[rb][t][i] = (32 * t + i < lim) ? sacc[rb][t][i] : -__builtin_inff();
       }
-      // row maximum: four independent chains, then the partner lane
-      float m4[4];
+      // P against the current reference maximum, and its row sum: for fp16
+      // from the rounded P on the matrix cores, for bf16 the lane's fp32
+      // partial sum. A sum within kTileSumLimit bounds every P of the row, so
+      // no maximum is needed on this path. Otherwise (always on a row's first
+      // tile, where m_run = -inf, and whenever the scores have grown past the
+      // reference by about 2^15) the row maximum is taken, O and l are
+      // rescaled to it and P is redone. The test is wave-wide, so the rare
+      // path stays out of the common one as a scalar branch.
+      float lsum = tile_sum(exp_tile(sacc[rb], -m_run[rb], pf[rb]), pf[rb]);
+      if (__any(!(lsum <= kTileSumLimit))) {
+        float m4[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) m4[k] = sacc[rb][0][k];
+        for (int k = 0; k < 4; ++k) m4[k] = sacc[rb][0][k];
 #pragma unroll
-      for (int t = 0; t < NSUB; ++t)
+        for (int t = 0; t < NSUB; ++t)
 #pragma unroll
-        for (int i = (t == 0 ? 4 : 0); i < 16; ++i) m4[i & 3] = fmaxf(m4[i & 3], sacc[rb][t][i]);
-      const float mx = max_with_partner(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * c;
-      // P against the current reference maximum. Only when the tile exceeds
-      // it by more than the slack (always on the first visible tile, where
-      // m_run = -inf) is the maximum raised, O and l rescaled and P redone;
-      // keeping that rare path out of the common one lets the common path
-      // stay a single block for the scheduler.
-      float lsum = exp_tile(sacc[rb], -m_run[rb], pf[rb]);
-      if (__any(mx > m_run[rb] + kRescaleSlack)) {
-        float m_new = fmaxf(m_run[rb], mx);
+          for (int i = (t == 0 ? 4 : 0); i < 16; ++i) m4[i & 3] = vmax(m4[i & 3], sacc[rb][t][i]);
+        const float mx = max_with_partner(vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3]))) * c;
+        float m_new = vmax(m_run[rb], mx);
         m_new = (m_new == -__builtin_inff()) ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
 #pragma unroll
@@ -502,9 +510,8 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[rb][t][i] *= alpha;
         l_run[rb] *= alpha;
-        if constexpr (M::kMfmaRowSum) lacc[rb] *= alpha;
         m_run[rb] = m_new;
-        lsum = exp_tile(sacc[rb], -m_new, pf[rb]);
+        lsum = tile_sum(exp_tile(sacc[rb], -m_new, pf[rb]), pf[rb]);
       }
       l_run[rb] += lsum;
     }
@@ -527,15 +534,6 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             if (act[rb]) oacc[rb][dt] = M::run(a, pf[rb][t][s2], oacc[rb][dt]);
-          if constexpr (M::kMfmaRowSum) {
-            if (dt == 0) {
-#pragma unroll
-              for (int rb = 0; rb < RB; ++rb)
-                if (act[rb])
-                  lacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                      row_sel, __builtin_bit_cast(f16x8, pf[rb][t][s2]), lacc[rb], 0, 0, 0);
-            }
-          }
         }
   };
 
@@ -583,7 +581,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int q_row = wave_q0 + 32 * rb + r32;
-    const float l_tot = M::kMfmaRowSum ? lacc[rb][0] : sum_with_partner(l_run[rb]);
+    const float l_tot = M::kMfmaRowSum ? l_run[rb] : sum_with_partner(l_run[rb]);
     const float inv = 1.0f / l_tot;
     if (q_row < Nq) {
       T* Oh = (T*)p.o + q_head + (size_t)q_row * D;
