@@ -33,7 +33,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into libfa.so next to this file; return its path."""
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-o", tmp] + SOURCES

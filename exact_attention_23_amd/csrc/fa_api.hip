@@ -23,27 +23,27 @@ struct Variant {
 };
 
 // Tile shapes per head width: NW waves of RB 32-row blocks, BN keys per tile,
-// S LDS stages.
-template <int D, int BN, int NW, int RB, int S, typename T>
+// S LDS stages, and whether the software-pipelined loop is used.
+template <int D, int BN, int NW, int RB, int S, bool PIPE, typename T>
 Variant make_variant(bool causal) {
   Variant v;
-  v.fn = causal ? fa::fa_fwd_kernel<D, BN, NW, RB, S, true, T>
-                : fa::fa_fwd_kernel<D, BN, NW, RB, S, false, T>;
+  v.fn = causal ? fa::fa_fwd_kernel<D, BN, NW, RB, S, PIPE, true, T>
+                : fa::fa_fwd_kernel<D, BN, NW, RB, S, PIPE, false, T>;
   v.bm = 32 * RB * NW;
   v.threads = 64 * NW;
   return v;
 }
 
-// Tile configuration per head width as (D, BN, NW, RB, S). A build can
-// override them with -DFA_TILES_D32=... etc. to compare configurations.
+// Tile configuration per head width as (D, BN, NW, RB, S, PIPE). A build
+// can override them with -DFA_TILES_D32=... etc. to compare configurations.
 #ifndef FA_TILES_D32
-#define FA_TILES_D32 32, 64, 4, 2, 4
+#define FA_TILES_D32 32, 64, 4, 2, 4, true
 #endif
 #ifndef FA_TILES_D64
-#define FA_TILES_D64 64, 64, 4, 1, 4
+#define FA_TILES_D64 64, 64, 4, 1, 4, false
 #endif
 #ifndef FA_TILES_D128
-#define FA_TILES_D128 128, 64, 8, 1, 4
+#define FA_TILES_D128 128, 64, 8, 1, 4, false
 #endif
 
 template <typename T>

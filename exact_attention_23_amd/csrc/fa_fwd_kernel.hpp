@@ -51,7 +51,6 @@
 //     row sum carry the same reference. The common path thus needs no row
 //     maximum at all: per score it is one FMA, one exp2 and half a conversion.
 #pragma once
-
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -223,7 +222,7 @@ __device__ __forceinline__ void work_item(const Params& p, int bid, int& head, i
   qb = CAUSAL ? (p.num_qb - 1 - rank) : rank;
 }
 
-template <int D, int BN, int NW, int RB, int S, bool CAUSAL, typename T>
+template <int D, int BN, int NW, int RB, int S, bool PIPE, bool CAUSAL, typename T>
 __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   using M = Mma<T>;
   using vec = typename M::vec;
@@ -250,7 +249,8 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   static_assert(S >= 3 && PENDING < 64, "stage count out of range");
 
   // K and V tiles as loaded ([stage][K,V], rows = keys), and V^T tiles
-  // (rows = d, BN keys each) for the P V operand, double-buffered.
+  // (rows = d, BN keys each) for the P V operand, double-buffered: while
+  // tile j runs, V^T of tile j+1 is written.
   __shared__ __attribute__((aligned(1024))) char smem[S][2][TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vts[2][TILE_BYTES];
 
@@ -404,137 +404,134 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
     for (int i = 0; i < TPW; ++i) *(i16x4*)(vdst + tr_dst[i]) = blk[i];
   };
 
-  // Row block rb sees some key of tile j unless the tile starts after its
-  // last row (causal); such blocks skip the tile.
-  auto active = [&](int j, int rb) { return !CAUSAL || j * BN <= wave_q0 + 32 * rb + 31; };
+  // The work is a sequence of units, one per 32-key subtile t of tile j
+  // (unit u = 2j + t). Registers per unit: its scores, its P (B operands) and
+  // its row sum, double-buffered by t.
+  static_assert(NSUB == 2, "a tile is two 32-key units");
+  f32x16 sacc[2][RB];
+  vec pf[2][RB][2];
+  float psum[2][RB];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      psum[b][rb] = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) pf[b][rb][s2] = vec{};
+    }
 
-  // ---- S^T = K Q^T for the BN keys of tile j (K from its LDS stage)
-  auto qk = [&](int j, f32x16 (&sacc)[RB][NSUB]) {
+  // LDS operands of one unit: K rows of subtile t of tile j (A operands of
+  // S^T = K Q^T, one per k-step) and V^T of subtile t of tile j (A operands
+  // of O^T += V^T P^T, per 16-key half s2 and 32-wide d tile).
+  auto load_k = [&](int j, int t, vec (&kf)[KS]) {
     const char* ks = smem[j % S][0];
-    const f32x16 zero = {};
-    // k-step outer, subtile inner: consecutive MFMAs feed different accumulators
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kf[s] = *(const vec*)(ks + k_roff[t][s]);
+  };
+  auto load_v = [&](int j, int t, vec (&vf)[2][NDT]) {
+    const char* vs = vts[j & 1];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) vf[s2][dt] = *(const vec*)(vs + v_roff[dt][t][s2]);
+  };
+  auto qk = [&](const vec (&kf)[KS], f32x16 (&out)[RB]) {
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int t = 0; t < NSUB; ++t) {
-        const vec a = *(const vec*)(ks + k_roff[t][s]);
+      for (int rb = 0; rb < RB; ++rb) out[rb] = M::run(kf[s], qf[rb][s], s == 0 ? f32x16{} : out[rb]);
+  };
+  auto pv = [&](const vec (&vf)[2][NDT], const vec (&pr)[RB][2]) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          sacc[rb][t] = M::run(a, qf[rb][s], s == 0 ? zero : sacc[rb][t]);
-      }
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) oacc[rb][dt] = M::run(vf[s2][dt], pr[rb][s2], oacc[rb][dt]);
   };
 
-  // P = 2^(S*c - m) for one row block, rounded in pairs into B operands;
-  // returns this tile's contribution to the row sum.
-  auto exp_tile = [&](const f32x16 (&sr)[NSUB], float negm, vec (&pr)[NSUB][2]) {
-    float lsum = 0.f;
+  // Scores of keys past Nk, and (causal) of keys after the row, -> -inf.
+  // Rows past a causal row block's last row are masked too, so such tiles
+  // add exact zeros.
+  auto mask_unit = [&](int j, int t, f32x16 (&sr)[RB]) {
 #pragma unroll
-    for (int t = 0; t < NSUB; ++t) {
-      u32x4 w0, w1;
+    for (int rb = 0; rb < RB; ++rb) {
+      // keys j*BN + 32t + 16*half + i are visible while i < lim
+      const int q_row = wave_q0 + 32 * rb + r32;
+      int lim = CAUSAL ? (q_row + 1 < Nk ? q_row + 1 : Nk) : Nk;
+      lim -= j * BN + 32 * t + 16 * half;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[t][2 * i], c, negm));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[t][2 * i + 1], c, negm));
-        const pair pp = M::cvt(p0, p1);
-        lsum = M::row_sum(p0, p1, pp, lsum);
-        if (i < 4) w0[i] = __builtin_bit_cast(uint32_t, pp);
-        else w1[i - 4] = __builtin_bit_cast(uint32_t, pp);
-      }
-      pr[t][0] = __builtin_bit_cast(vec, w0);
-      pr[t][1] = __builtin_bit_cast(vec, w1);
+      for (int i = 0; i < 16; ++i) sr[rb][i] = (i < lim) ? sr[rb][i] : -__builtin_inff();
     }
-    return lsum;
   };
 
-  // Row sum of a tile's P: for fp16, four 16x16x32 MFMAs of the selector
+  // Row sum of a unit's P: for fp16, two 16x16x32 MFMAs of the selector
   // against the rounded P (each lane gets its own query's sum); for bf16 the
-  // fp32 partial sum exp_tile returned.
-  auto tile_sum = [&](float lsum, const vec (&pr)[NSUB][2]) -> float {
+  // fp32 partial sum accumulated while P was formed.
+  auto sub_sum = [&](float lsum, const vec (&pr)[2]) -> float {
     if constexpr (M::kMfmaRowSum) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < NSUB; ++t)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(row_sel, __builtin_bit_cast(f16x8, pr[t][s2]),
-                                                       acc, 0, 0, 0);
+      for (int s2 = 0; s2 < 2; ++s2)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(row_sel, __builtin_bit_cast(f16x8, pr[s2]), acc,
+                                                     0, 0, 0);
       return acc[0];
     } else {
       return lsum;
     }
   };
 
-  // ---- online softmax of tile j's scores -> P (fp16/bf16 B operands); O and
-  // the row sum are rescaled when the reference maximum is raised. MASK
-  // selects the instantiation for tiles that need tail or causal masking.
-  auto softmax = [&](auto mask_tag, int j, f32x16 (&sacc)[RB][NSUB], vec (&pf)[RB][NSUB][2]) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const int kb = j * BN;
+  // P = 2^(S*c - m) of one row block's unit, rounded in pairs into its two B
+  // operands; returns its row sum.
+  auto exp_unit = [&](const f32x16& sr, float negm, vec (&pr)[2]) {
+    float lsum = 0.f;
+    u32x4 w[2];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      if (!active(j, rb)) continue;
-      if (MASK) {
-        // keys kb + 32t + 16*half + i are visible while i < lim - 32t
-        const int q_row = wave_q0 + 32 * rb + r32;
-        int lim = CAUSAL ? (q_row + 1 < Nk ? q_row + 1 : Nk) : Nk;
-        lim -= kb + 16 * half;
-#pragma unroll
-        for (int t = 0; t < NSUB; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            sacc[rb][t][i] = (32 * t + i < lim) ? sacc[rb][t][i] : -__builtin_inff();
-      }
-      // P against the current reference maximum, and its row sum: for fp16
-      // from the rounded P on the matrix cores, for bf16 the lane's fp32
-      // partial sum. A sum within kTileSumLimit bounds every P of the row, so
-      // no maximum is needed on this path. Otherwise (always on a row's first
-      // tile, where m_run = -inf, and whenever the scores have grown past the
-      // reference by about 2^15) the row maximum is taken, O and l are
-      // rescaled to it and P is redone. The test is wave-wide, so the rare
-      // path stays out of the common one as a scalar branch.
-      float lsum = tile_sum(exp_tile(sacc[rb], -m_run[rb], pf[rb]), pf[rb]);
-      if (__any(!(lsum <= kTileSumLimit))) {
-        float m4[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) m4[k] = sacc[rb][0][k];
-#pragma unroll
-        for (int t = 0; t < NSUB; ++t)
-#pragma unroll
-          for (int i = (t == 0 ? 4 : 0); i < 16; ++i) m4[i & 3] = vmax(m4[i & 3], sacc[rb][t][i]);
-        const float mx = max_with_partner(vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3]))) * c;
-        float m_new = vmax(m_run[rb], mx);
-        m_new = (m_new == -__builtin_inff()) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
-#pragma unroll
-        for (int t = 0; t < NDT; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[rb][t][i] *= alpha;
-        l_run[rb] *= alpha;
-        m_run[rb] = m_new;
-        lsum = tile_sum(exp_tile(sacc[rb], -m_new, pf[rb]), pf[rb]);
-      }
-      l_run[rb] += lsum;
+    for (int i = 0; i < 8; ++i) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[2 * i], c, negm));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[2 * i + 1], c, negm));
+      const pair pp = M::cvt(p0, p1);
+      lsum = M::row_sum(p0, p1, pp, lsum);
+      w[i >> 2][i & 3] = __builtin_bit_cast(uint32_t, pp);
     }
+    pr[0] = __builtin_bit_cast(vec, w[0]);
+    pr[1] = __builtin_bit_cast(vec, w[1]);
+    return sub_sum(lsum, pr);
   };
 
-  // ---- O^T += V^T P^T for tile j (V^T from its transposed buffer)
-  auto pv = [&](int j, vec (&pf)[RB][NSUB][2]) {
-    const char* vs = vts[j & 1];
-    bool act[RB];
+  // Row maximum of a unit's scores, in the exp2 domain (both lanes of the
+  // row take part).
+  auto unit_max = [&](const f32x16& sr) -> float {
+    float m4[4];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) act[rb] = active(j, rb);
-    // key chunk outer, d tile inner: consecutive MFMAs feed different accumulators
+    for (int k = 0; k < 4; ++k) m4[k] = sr[k];
 #pragma unroll
-    for (int t = 0; t < NSUB; ++t)
+    for (int i = 4; i < 16; ++i) m4[i & 3] = vmax(m4[i & 3], sr[i]);
+    return max_with_partner(vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3]))) * c;
+  };
+  // Raise row block rb's reference maximum to cover mx: O and l are rescaled
+  // by 2^(m_old - m_new). A row with no visible key yet keeps 0.
+  auto raise_max = [&](int rb, float mx) {
+    float m_new = vmax(m_run[rb], mx);
+    m_new = (m_new == -__builtin_inff()) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const vec a = *(const vec*)(vs + v_roff[dt][t][s2]);
+      for (int i = 0; i < 16; ++i) oacc[rb][dt][i] *= alpha;
+    l_run[rb] *= alpha;
+    m_run[rb] = m_new;
+  };
+  // A unit's row sum bounds every P of the row, so a sum within
+  // kTileSumLimit means its P is finite in fp16 and was formed against a
+  // usable reference (no maximum is needed for that). Otherwise (a row's
+  // first unit, where m_run = -inf, or scores grown past the reference by
+  // about 2^15) the reference is raised and P redone.
+  auto unit_ok = [&](const float (&ps)[RB]) {
+    bool ok = true;
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            if (act[rb]) oacc[rb][dt] = M::run(a, pf[rb][t][s2], oacc[rb][dt]);
-        }
+    for (int rb = 0; rb < RB; ++rb) ok &= (ps[rb] <= kTileSumLimit);
+    return ok;
   };
 
   // Tiles from `first_masked` on need masking: the tile holding key Nk-1 when
@@ -547,35 +544,174 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   }
   first_masked = first_masked < ntiles ? first_masked : ntiles;
 
-  // Pipeline. Tiles 0..S-2 are requested up front; iteration j requests tile
-  // j+S-1 into the stage of tile j-1 (free since the last barrier), writes
-  // V^T of tile j+1 (its stage has landed), runs QK^T, softmax and P V of
-  // tile j (V^T of tile j was written before the last barrier), then waits
-  // until tile j+2 has landed (its own loads) and meets the other waves at the
-  // barrier. Past the last tile the stages hold zeros from out-of-range loads.
+  // Start of tile j (both loops): request tile j+S-1 into the stage of tile
+  // j-1 (free since the last barrier) and write V^T of tile j+1 (its stage
+  // has landed). End of tile j: wait until tile j+2 has landed (this wave's
+  // own loads) and meet the other waves at the barrier. Past the last tile
+  // the stages hold zeros from out-of-range loads.
+  auto tile_start = [&](int j) {
+    issue(j + S - 1);
+    transpose_v(j + 1);
+  };
+  auto tile_end = [&]() {
+    wait_vmcnt<PENDING>();
+    __syncthreads();
+  };
+
+  // ---- the plain loop: one tile at a time. Q K^T of both units, mask, P
+  // and row sums, one acceptance test for the tile (raising the reference to
+  // the tile's maximum when it fails), then P V.
+  auto plain_tile = [&](auto mask_tag, int j) {
+    {
+      // k-step outer, unit inner: consecutive MFMAs feed different
+      // accumulators
+      const char* ks = smem[j % S][0];
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const vec a = *(const vec*)(ks + k_roff[t][s]);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            sacc[t][rb] = M::run(a, qf[rb][s], s == 0 ? f32x16{} : sacc[t][rb]);
+        }
+    }
+    if (decltype(mask_tag)::value) {
+      mask_unit(j, 0, sacc[0]);
+      mask_unit(j, 1, sacc[1]);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) psum[t][rb] = exp_unit(sacc[t][rb], -m_run[rb], pf[t][rb]);
+    if (__any(!(unit_ok(psum[0]) && unit_ok(psum[1])))) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        raise_max(rb, vmax(unit_max(sacc[0][rb]), unit_max(sacc[1][rb])));
+#pragma unroll
+        for (int t = 0; t < 2; ++t) psum[t][rb] = exp_unit(sacc[t][rb], -m_run[rb], pf[t][rb]);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) l_run[rb] += psum[0][rb] + psum[1][rb];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      vec vf[2][NDT];
+      load_v(j, t, vf);
+      pv(vf, pf[t]);
+    }
+    tile_end();
+  };
+
+  // ---- the pipelined loop: Q K^T runs one unit ahead. Unit u forms its P
+  // on the vector units while the matrix cores compute the scores of unit
+  // u+1; the order is written out (each MFMA, then its share of the P pairs,
+  // fenced so that the compiler keeps the interleaving). Then come unit u's
+  // row sums on the matrix cores, its acceptance test (raising the reference
+  // and redoing P when it fails) and its P V. Only the scores cross from one
+  // unit to the next.
+  constexpr int NMF = RB * KS;  // Q K^T MFMAs of a unit
+  constexpr int NPR = RB * 8;   // P pairs of a unit
+  auto piped_unit = [&](auto mask_tag, int j, int t, f32x16 (&sr)[RB], vec (&pr)[RB][2],
+                        float (&ps)[RB], const vec (&kf)[KS], f32x16 (&sn)[RB]) {
+    if (decltype(mask_tag)::value) mask_unit(j, t, sr);
+    float negm[RB], lsum[RB];
+    u32x4 w[RB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      negm[rb] = -m_run[rb];
+      lsum[rb] = 0.f;
+    }
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (
+          [&] {
+            constexpr int m = I;
+            constexpr int s = m / RB, rb = m % RB;
+            sn[rb] = M::run(kf[s], qf[rb][s], s == 0 ? f32x16{} : sn[rb]);
+#pragma unroll
+            for (int q = m * NPR / NMF; q < (m + 1) * NPR / NMF; ++q) {
+              const int rq = q / 8, i = q % 8;
+              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[rq][2 * i], c, negm[rq]));
+              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[rq][2 * i + 1], c, negm[rq]));
+              const pair pq = M::cvt(p0, p1);
+              lsum[rq] = M::row_sum(p0, p1, pq, lsum[rq]);
+              w[rq][i >> 2][i & 3] = __builtin_bit_cast(uint32_t, pq);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }(),
+          ...);
+    }(std::make_integer_sequence<int, NMF>{});
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      pr[rb][0] = __builtin_bit_cast(vec, w[rb][0]);
+      pr[rb][1] = __builtin_bit_cast(vec, w[rb][1]);
+      ps[rb] = sub_sum(lsum[rb], pr[rb]);
+    }
+    vec vf[2][NDT];
+    load_v(j, t, vf);
+    if (__any(!unit_ok(ps))) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        raise_max(rb, unit_max(sr[rb]));
+        ps[rb] = exp_unit(sr[rb], -m_run[rb], pr[rb]);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) l_run[rb] += ps[rb];
+    pv(vf, pr);
+  };
+  auto piped_tile = [&](auto mask_tag, int j) {
+    {  // unit (j, 0), with Q K^T of unit (j, 1)
+      vec kf[KS];
+      load_k(j, 1, kf);
+      piped_unit(mask_tag, j, 0, sacc[0], pf[0], psum[0], kf, sacc[1]);
+    }
+    {  // unit (j, 1), with Q K^T of unit (j+1, 0)
+      vec kf[KS];
+      load_k(j + 1, 0, kf);
+      piped_unit(mask_tag, j, 1, sacc[1], pf[1], psum[1], kf, sacc[0]);
+    }
+    tile_end();
+  };
+
+  // ---- prologue: tiles 0..S-2 requested, V^T of tile 0 written.
 #pragma unroll
   for (int t = 0; t < S - 1; ++t) issue(t);
   wait_vmcnt<PENDING>();
   __syncthreads();
   transpose_v(0);
   __syncthreads();
-  vec pf[RB][NSUB][2];
-  f32x16 sc[RB][NSUB];
-  auto step = [&](auto mask_tag, int j) {
-    issue(j + S - 1);
-    transpose_v(j + 1);
-    qk(j, sc);
-    __builtin_amdgcn_sched_barrier(0);
-    softmax(mask_tag, j, sc, pf);
-    pv(j, pf);
-    wait_vmcnt<PENDING>();
-    __syncthreads();
-  };
-  // Two loops rather than a per-tile branch, so the accumulators keep one
-  // register assignment through the interior tiles.
+
+  const auto unmasked = std::integral_constant<bool, false>{};
+  const auto masked = std::integral_constant<bool, true>{};
   int j = 0;
-  for (; j < first_masked; ++j) step(std::integral_constant<bool, false>{}, j);
-  for (; j < ntiles; ++j) step(std::integral_constant<bool, true>{}, j);
+  if constexpr (PIPE) {
+    // Scores of unit (0, 0) before the loop; the first unit's test raises
+    // the reference from -inf.
+    {
+      vec kf[KS];
+      load_k(0, 0, kf);
+      qk(kf, sacc[0]);
+    }
+    for (; j < first_masked; ++j) {
+      tile_start(j);
+      piped_tile(unmasked, j);
+    }
+    for (; j < ntiles; ++j) {
+      tile_start(j);
+      piped_tile(masked, j);
+    }
+  }
+  if constexpr (!PIPE) {
+    for (; j < first_masked; ++j) {
+      tile_start(j);
+      plain_tile(unmasked, j);
+    }
+    for (; j < ntiles; ++j) {
+      tile_start(j);
+      plain_tile(masked, j);
+    }
+  }
 
   // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
 #pragma unroll

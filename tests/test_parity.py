@@ -89,6 +89,43 @@ def test_large_logits_tail():
             compare(o, lse, O, L, what=f"large logits d={d} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_reference_raised_midway(d, dtype):
+    """Keys whose scores jump far above everything before them, placed in the
+    first and in the second 32-key half of different tiles, so the running
+    reference maximum has to be raised in the middle of the key range (and
+    repeatedly), not only on the first tile."""
+    require_gpu()
+    note(f"parity raised reference d={d} {dtype}")
+    q, k, v = rand_inputs(1, 2, 300, 400, d, dtype, seed=900 + d, v_uniform=True)
+    q = (q.float().abs() + 0.5).to(q.dtype)  # every query row sees the jumps
+    k = k.float()
+    for pos, height in ((37, 2.0), (69, 4.0), (130, 5.0), (230, 7.0), (333, 9.0)):
+        k[:, :, pos, :] = height
+    k = k.to(q.dtype)
+    for causal in (False, True):
+        o, lse = run_gpu(q, k, v, causal)
+        O, L = oracle.attention(q, k, v, scale=default_scale(d), causal=causal)
+        compare(o, lse, O, L, what=f"raised reference d={d} {dtype} causal={causal}")
+
+
+def test_rising_scores():
+    """Scores that grow steadily along the keys: the reference falls behind
+    on many tiles of every row block."""
+    require_gpu()
+    note("parity rising scores")
+    for d in (32, 64, 128):
+        q, k, v = rand_inputs(2, 1, 260, 700, d, "fp16", seed=31 + d, v_uniform=True)
+        q = (q.float().abs() * 0.5 + 0.5).to(q.dtype)
+        ramp = torch.linspace(0.0, 6.0, 700).view(1, 1, 700, 1)
+        k = (k.float() * 0.2 + ramp).to(k.dtype)
+        for causal in (False, True):
+            o, lse = run_gpu(q, k, v, causal)
+            O, L = oracle.attention(q, k, v, scale=default_scale(d), causal=causal)
+            compare(o, lse, O, L, what=f"rising scores d={d} causal={causal}")
+
+
 SAMPLE_ROWS = 48
 
 
