@@ -16,6 +16,11 @@ FA_ERR_CAUSAL = 6
 FA_ERR_ALIGN = 7
 FA_ERR_ALIAS = 8
 FA_ERR_LAUNCH = 9
+FA_ERR_PATH = 10
+
+FA_PATH_AUTO = 0
+FA_PATH_TILED = 1
+FA_PATH_SHORT = 2
 
 FA_DTYPE_FP16 = 0
 FA_DTYPE_BF16 = 1
@@ -48,6 +53,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                            ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
     lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                              ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    lib.fa_fwd_ex.restype = ctypes.c_int
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_launch_error.argtypes = []

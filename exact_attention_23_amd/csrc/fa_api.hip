@@ -9,6 +9,7 @@
 
 #include "../../include/fa.h"
 #include "fa_fwd_kernel.hpp"
+#include "fa_fwd_short.hpp"
 
 namespace {
 
@@ -55,6 +56,36 @@ Variant pick(int64_t d, bool causal) {
   }
 }
 
+// The short-range kernel for one head width: its launch function and the most
+// 64-key tiles it takes.
+template <typename T>
+struct ShortVariant {
+  KernelFn fn;
+  int max_tiles;
+};
+template <int D, typename T>
+ShortVariant<T> make_short(bool causal) {
+  return {causal ? fa::fa_fwd_short_kernel<D, true, T> : fa::fa_fwd_short_kernel<D, false, T>,
+          fa::kShortMaxWaves<D>};
+}
+template <typename T>
+ShortVariant<T> pick_short(int64_t d, bool causal) {
+  switch (d) {
+    case 32: return make_short<32, T>(causal);
+    case 64: return make_short<64, T>(causal);
+    default: return make_short<128, T>(causal);
+  }
+}
+
+// Compute units of the current device (the tiled path fills them only
+// with at least this many workgroups).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 256;
+  return n > 0 ? n : 256;
+}
+
 // HIP's description of the last failed launch on this thread.
 thread_local const char* g_launch_error = "";
 
@@ -83,6 +114,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_ALIAS: return "o or lse overlaps an input or each other";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_PATH: return "unknown path, or the short path with too many keys for it";
     default: return "unknown status";
   }
 }
@@ -90,6 +122,12 @@ const char* fa_status_str(int status) {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
            float scale, int causal, int dtype, void* stream) {
+  return fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, FA_PATH_AUTO, stream);
+}
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+              float scale, int causal, int dtype, int path, void* stream) {
   // ---- every check happens before the first HIP call
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_NULLPTR;
   if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
@@ -123,6 +161,17 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
       (overlaps(lse, lse_bytes, q, qo_bytes) || overlaps(lse, lse_bytes, k, kv_bytes) ||
        overlaps(lse, lse_bytes, v, kv_bytes) || overlaps(lse, lse_bytes, o, qo_bytes)))
     return FA_ERR_ALIAS;
+  if (path != FA_PATH_AUTO && path != FA_PATH_TILED && path != FA_PATH_SHORT) return FA_ERR_PATH;
+  const int64_t key_tiles = (Nk + 63) / 64;
+  const int short_max = d == 128 ? fa::kShortMaxWaves<128> : fa::kShortMaxWaves<64>;
+  const bool short_fits = key_tiles <= short_max;
+  if (path == FA_PATH_SHORT && !short_fits) return FA_ERR_PATH;
+  const int64_t short_total = B * H * ((Nq + 31) / 32);
+  if (short_total >= lim) return FA_ERR_SHAPE;
+  // Latency-bound sizes: the short path's workgroups (one per 32 rows, at
+  // most one per compute unit for its LDS) all run at once.
+  const bool use_short =
+      path == FA_PATH_SHORT || (path == FA_PATH_AUTO && short_fits && short_total <= device_cus());
 
   fa::Params p;
   p.q = q;
@@ -139,6 +188,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   p.xcd_q = (int)(total / 8);
   p.xcd_r = (int)(total % 8);
   p.group = 1;
+  p.nkt = (int)key_tiles;
   if (scale == 0.0f) {  // every logit is 0: zero Q, any positive factor works
     p.c = 1.0f;
     p.q_and = 0u;
@@ -150,8 +200,18 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   }
 
   void* args[] = {&p};
-  hipError_t e = hipLaunchKernel((const void*)var.fn, dim3((unsigned)total), dim3(var.threads),
-                                 args, 0, (hipStream_t)stream);
+  hipError_t e;
+  if (use_short) {
+    const KernelFn fn = dtype == FA_DTYPE_FP16 ? pick_short<_Float16>(d, causal != 0).fn
+                                               : pick_short<__bf16>(d, causal != 0).fn;
+    p.num_qb = (int)((Nq + 31) / 32);
+    p.total = (int)short_total;
+    e = hipLaunchKernel((const void*)fn, dim3((unsigned)short_total), dim3((unsigned)(64 * key_tiles)),
+                        args, 0, (hipStream_t)stream);
+  } else {
+    e = hipLaunchKernel((const void*)var.fn, dim3((unsigned)total), dim3(var.threads), args, 0,
+                        (hipStream_t)stream);
+  }
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess) {
     g_launch_error = hipGetErrorString(e);

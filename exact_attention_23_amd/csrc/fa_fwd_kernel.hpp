@@ -86,6 +86,7 @@ struct Params {
   float c;        // |scale| * log2(e), or 1 when scale == 0
   uint32_t q_and; // applied to each 32-bit word of Q: ~0 normally, 0 when scale == 0
   uint32_t q_xor; // 0x80008000 flips both halves' sign when scale < 0
+  int nkt;        // short-range kernel: 64-key tiles (= waves) per workgroup
 };
 
 // Largest tile row sum, relative to the reference maximum, that is accepted

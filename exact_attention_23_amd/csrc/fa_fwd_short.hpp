@@ -1,0 +1,247 @@
+// fa_fwd_short.hpp - the exact-attention forward for short key ranges on
+// gfx950: the keys of a head are split over the waves of one workgroup.
+//
+// Method: the same attention, and the same exactness argument, as the tiled
+// kernel (kwkr.cn YOLO11 FlashAttention-2 article, section 1.2; "FlashAttention
+// 深度解读", section 原理 items 1-2). A row's softmax over its keys is the
+// combination of softmaxes over disjoint key ranges: with per-range maxima
+// m_w, sums l_w and unnormalised outputs O_w, the row's maximum is
+// M = max_w m_w, its sum L = sum_w 2^(m_w - M) l_w and its output
+// O = sum_w 2^(m_w - M) O_w / L (exp2 domain). The pages' online update is the
+// sequential form of this combination; here it runs in parallel.
+//
+// gfx950 mapping
+//   * A workgroup owns 32 query rows of one (batch, head) and one wave per
+//     64-key tile of the head (up to kShortMaxWaves), so a short sequence is
+//     a single tile deep: its latency is one tile, not Nk/64 tiles in turn.
+//   * Each wave reads its K rows straight from global memory as MFMA A
+//     operands (in the permuted key order that makes the score accumulators
+//     the P operand, as in the tiled kernel) and its V tile into its own LDS
+//     region; the V^T operands of P V come from that region through
+//     ds_read_b64_tr_b16 (two transpose reads give the 8 keys of a fragment).
+//   * Each wave takes the exact maximum of its tile, forms P = 2^(S*c - m_w)
+//     (at most 1), its row sum (fp16: on the matrix cores from the rounded P;
+//     bf16: in fp32) and O_w. The waves then exchange m_w and l_w through LDS,
+//     scale their O_w by 2^(m_w - M) into their LDS regions, and all threads
+//     sum the partials, normalise and store O and LSE.
+#pragma once
+
+#include "fa_fwd_kernel.hpp"
+
+namespace fa {
+
+// Most 64-key tiles (one wave each) a short-range workgroup takes; LDS holds
+// one V tile, later one fp32 partial O, per wave.
+template <int D>
+constexpr int kShortMaxWaves = D == 128 ? 9 : 16;
+
+template <int D, bool CAUSAL, typename T>
+__global__ __launch_bounds__(1024) void fa_fwd_short_kernel(Params p) {
+  using M = Mma<T>;
+  using vec = typename M::vec;
+  using pair = typename M::pair;
+  constexpr int KS = D / 16;    // k-steps of the QK^T contraction
+  constexpr int NDT = D / 32;   // 32-wide d tiles of O
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  constexpr int MAXW = kShortMaxWaves<D>;
+  constexpr int PS = D + 4;                 // floats per row of a partial O (padded)
+  constexpr int REGION = 32 * PS * 4;       // per-wave LDS bytes: partial O ...
+  static_assert(REGION >= 64 * D * 2, "... and, before it, the wave's V tile");
+  __shared__ __attribute__((aligned(1024))) char smem[MAXW * REGION];
+  __shared__ float s_m[MAXW][32], s_l[MAXW][32], s_M[32], s_L[32];
+
+  const int head = blockIdx.x / p.num_qb;
+  const int qb = blockIdx.x - head * p.num_qb;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // scalar wave index: every per-wave choice below is a scalar branch
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int r32 = lane & 31;
+  const int Nq = p.Nq, Nk = p.Nk, nw = p.nkt;
+
+  const size_t q_head = (size_t)head * Nq * D;
+  const size_t kv_head = (size_t)head * Nk * D;
+  const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const T*)p.q + q_head), (short)0, Nq * D * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const T*)p.k + kv_head), (short)0, Nk * D * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const T*)p.v + kv_head), (short)0, Nk * D * 2, kBufferFlags);
+
+  const int q0 = qb * 32;
+  const int q_row = q0 + r32;
+  const int kb = wave * 64;  // this wave's first key
+  char* vreg = smem + wave * REGION;
+
+  // ---- this wave's V tile (64 keys, rows past Nk read as zero) -> its LDS
+  // region, rows XOR-swizzled in 16-byte chunks as in the tiled kernel
+  {
+    const uint32_t lds_v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)vreg;
+#pragma unroll
+    for (int i = 0; i < CPR; ++i) {
+      const int sl = i * 64 + lane;
+      const int r = sl / CPR;
+      const int ch = (lds_off<2 * D>(r, sl % CPR) - r * (2 * D)) >> 4;  // logical chunk
+      dma_to_lds(v_rsrc, __builtin_amdgcn_readfirstlane(lds_v + i * 1024),
+                 (uint32_t)((kb + r) * (2 * D) + 16 * ch));
+    }
+  }
+
+  // ---- Q rows (B operands) and K rows (A operands, permuted key order)
+  vec qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, q_row * (2 * D) + 2 * (16 * s + 8 * half),
+                                                    0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = (w[e] & p.q_and) ^ p.q_xor;
+    qf[s] = __builtin_bit_cast(vec, w);
+  }
+  f32x16 sacc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int krow = kb + 32 * t + lds_row_to_key(r32);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const vec a = __builtin_bit_cast(
+          vec, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, krow * (2 * D) + 2 * (16 * s + 8 * half), 0, 0));
+      sacc[t] = M::run(a, qf[s], s == 0 ? f32x16{} : sacc[t]);
+    }
+  }
+
+  // ---- mask (keys past Nk; causal: keys after the row), exact maximum of
+  // the tile, P and its row sum
+  const float c = p.c;
+  {
+    int lim = CAUSAL ? (q_row + 1 < Nk ? q_row + 1 : Nk) : Nk;
+    lim -= kb + 16 * half;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[t][i] = (32 * t + i < lim) ? sacc[t][i] : -__builtin_inff();
+  }
+  float m;
+  {
+    float m4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m4[k] = vmax(sacc[0][k], sacc[1][k]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 4; i < 16; ++i) m4[i & 3] = vmax(m4[i & 3], sacc[t][i]);
+    m = max_with_partner(vmax(vmax(m4[0], m4[1]), vmax(m4[2], m4[3]))) * c;
+  }
+  const bool empty = m == -__builtin_inff();  // no visible key in this tile
+  const float negm = empty ? 0.f : -m;        // then every score is -inf and P = 0
+  vec pf[2][2];
+  float lsum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    u32x4 w[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][2 * i], c, negm));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][2 * i + 1], c, negm));
+      const pair pp = M::cvt(p0, p1);
+      lsum = M::row_sum(p0, p1, pp, lsum);
+      w[i >> 2][i & 3] = __builtin_bit_cast(uint32_t, pp);
+    }
+    pf[t][0] = __builtin_bit_cast(vec, w[0]);
+    pf[t][1] = __builtin_bit_cast(vec, w[1]);
+  }
+  float l;
+  if constexpr (M::kMfmaRowSum) {
+    // selector of the tiled kernel: lane l's sum lands in every register
+    const _Float16 sel_h =
+        (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? (_Float16)1.0f : (_Float16)0.0f;
+    const f16x8 row_sel = {sel_h, sel_h, sel_h, sel_h, sel_h, sel_h, sel_h, sel_h};
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(row_sel, __builtin_bit_cast(f16x8, pf[t][s2]), acc,
+                                                     0, 0, 0);
+    l = acc[0];
+  } else {
+    l = sum_with_partner(lsum);
+  }
+
+  // ---- O_w^T = V^T P^T. The V^T fragment for d tile dt, unit t, half s2 is
+  // d row 32*dt + lane%32 and keys 32t + 16*half + 8*s2 .. +7: two transpose
+  // reads, each handing lane x of a 16-lane group keys k0..k0+3 of column
+  // d0 + x while pointing at key k0 + x/4, columns d0 + 4*(x%4) .. +3.
+  wait_vmcnt<0>();  // this wave's V tile has landed (only this wave reads it)
+  f32x16 oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+  {
+    const int x = lane & 15;
+    const int d0b = 16 * ((lane >> 4) & 1);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int k0 = 32 * t + 16 * half + 8 * s2;
+          const int col = 32 * dt + d0b + 4 * (x & 3);
+          const int a0 = lds_off<2 * D>(k0 + (x >> 2), col >> 3) + 2 * (col & 7);
+          const int a1 = lds_off<2 * D>(k0 + 4 + (x >> 2), col >> 3) + 2 * (col & 7);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vreg + a0));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vreg + a1));
+          const u32x2 wl = __builtin_bit_cast(u32x2, lo), wh = __builtin_bit_cast(u32x2, hi);
+          const u32x4 w = {wl[0], wl[1], wh[0], wh[1]};
+          oacc[dt] = M::run(__builtin_bit_cast(vec, w), pf[t][s2], oacc[dt]);
+        }
+  }
+
+  // ---- combine the waves: M = max m_w, L = sum 2^(m_w - M) l_w
+  if (half == 0) {
+    s_m[wave][r32] = m;
+    s_l[wave][r32] = l;
+  }
+  __syncthreads();  // also: every wave is done with its V tile
+  float Mx = -__builtin_inff();
+  for (int w = 0; w < nw; ++w) Mx = vmax(Mx, s_m[w][r32]);
+  float L = 0.f;
+  for (int w = 0; w < nw; ++w) {
+    const float mw = s_m[w][r32];
+    L += mw == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mw - Mx) * s_l[w][r32];
+  }
+  const float alpha = empty ? 0.f : __builtin_amdgcn_exp2f(m - Mx);
+  // this wave's scaled partial O, rows = queries, in its own LDS region
+  float* part = (float*)vreg;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      part[r32 * PS + 32 * dt + 8 * (i >> 2) + 4 * half + (i & 3)] = oacc[dt][i] * alpha;
+  if (wave == 0 && half == 0) {
+    s_M[r32] = Mx;
+    s_L[r32] = L;
+  }
+  __syncthreads();
+
+  // ---- sum the partials (two adjacent d per thread), normalise, store
+  T* Oh = (T*)p.o + q_head;
+  for (int e = tid; e < 16 * D; e += 64 * nw) {
+    const int r = (2 * e) / D, d = (2 * e) % D;
+    if (q0 + r >= Nq) continue;
+    float a0 = 0.f, a1 = 0.f;
+    for (int w = 0; w < nw; ++w) {
+      const float* pw = (const float*)(smem + w * REGION) + r * PS + d;
+      a0 += pw[0];
+      a1 += pw[1];
+    }
+    const float inv = 1.0f / s_L[r];
+    *(pair*)(Oh + (size_t)(q0 + r) * D + d) = M::cvt(a0 * inv, a1 * inv);
+  }
+  if (p.lse != nullptr && tid < 32 && q0 + tid < Nq)
+    p.lse[(size_t)head * Nq + q0 + tid] = 0.69314718055994531f * (s_M[tid] + log2f(s_L[tid]));
+}
+
+}  // namespace fa

@@ -51,7 +51,9 @@ enum fa_status {
   FA_ERR_CAUSAL = 6,  /* causal not 0 or 1                                      */
   FA_ERR_ALIGN = 7,   /* q, k, v, o not 16-byte aligned, or lse not 4-byte      */
   FA_ERR_ALIAS = 8,   /* o or lse overlaps an input, or o overlaps lse          */
-  FA_ERR_LAUNCH = 9   /* the kernel launch itself failed (hipGetLastError)      */
+  FA_ERR_LAUNCH = 9,  /* the kernel launch itself failed (hipGetLastError)      */
+  FA_ERR_PATH = 10    /* fa_fwd_ex: unknown path, or FA_PATH_SHORT with Nk too  */
+                      /* large for it                                           */
 };
 
 /* Element types of q, k, v and o (all four share one type). Accumulation is
@@ -87,6 +89,35 @@ enum fa_dtype { FA_DTYPE_FP16 = 0, FA_DTYPE_BF16 = 1 };
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
            float scale, int causal, int dtype, void* stream);
+
+/* Kernel choice for fa_fwd_ex. Both compute the same operation; they differ
+ * in how the key range of a head is walked.
+ *   FA_PATH_TILED  one workgroup per block of query rows streams the head's
+ *                  keys tile after tile through LDS, updating the running
+ *                  maximum, sum and output as in the online softmax of the
+ *                  kwkr.cn YOLO11 FlashAttention-2 article, section 1.2.
+ *   FA_PATH_SHORT  for short key ranges: one workgroup per 32 query rows
+ *                  takes every 64-key tile at once, one wave per tile, and
+ *                  combines the per-tile maxima, sums and outputs exactly
+ *                  (the same rescaling, applied across tiles in parallel).
+ *                  Requires ceil(Nk / 64) <= 16 for d = 32 and 64, <= 9 for
+ *                  d = 128 (Nk <= 1024 or 576).
+ *   FA_PATH_AUTO   FA_PATH_SHORT when it applies and its workgroups
+ *                  (B*H*ceil(Nq/32)) are no more than the GPU's compute units,
+ *                  so they all run at once (latency-bound sizes);
+ *                  FA_PATH_TILED otherwise. */
+enum fa_path { FA_PATH_AUTO = 0, FA_PATH_TILED = 1, FA_PATH_SHORT = 2 };
+
+/*
+ * fa_fwd_ex - fa_fwd with an explicit kernel choice (fa_path). All other
+ * arguments, the results and the error behaviour are those of fa_fwd; an
+ * unknown path, or FA_PATH_SHORT beyond its key-range limit, returns
+ * FA_ERR_PATH after the other checks and before any HIP call.
+ * fa_fwd(...) is fa_fwd_ex(..., FA_PATH_AUTO, stream).
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+              float scale, int causal, int dtype, int path, void* stream);
 
 /* A static, human-readable description of a status code (never NULL). */
 const char* fa_status_str(int status);

@@ -29,10 +29,10 @@ def note(msg: str):
     print(msg, file=sys.stderr, flush=True)
 
 
-def run_gpu(q, k, v, causal, scale=None, with_lse=True):
+def run_gpu(q, k, v, causal, scale=None, with_lse=True, path="auto"):
     dev = torch.device("cuda:0")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    o, lse = fa.attention(qd, kd, vd, causal=causal, scale=scale, return_lse=with_lse)
+    o, lse = fa.attention(qd, kd, vd, causal=causal, scale=scale, return_lse=with_lse, path=path)
     torch.cuda.synchronize()
     return o.cpu(), (lse.cpu() if lse is not None else None)
 

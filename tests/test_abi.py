@@ -38,7 +38,8 @@ def test_header_enums_match_binding():
     src = _header_text()
     for name in ["FA_OK", "FA_ERR_NULLPTR", "FA_ERR_SHAPE", "FA_ERR_HEADDIM", "FA_ERR_DTYPE",
                  "FA_ERR_SCALE", "FA_ERR_CAUSAL", "FA_ERR_ALIGN", "FA_ERR_ALIAS", "FA_ERR_LAUNCH",
-                 "FA_DTYPE_FP16", "FA_DTYPE_BF16"]:
+                 "FA_ERR_PATH", "FA_DTYPE_FP16", "FA_DTYPE_BF16", "FA_PATH_AUTO", "FA_PATH_TILED",
+                 "FA_PATH_SHORT"]:
         m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
         assert m, name
         assert int(m.group(1)) == getattr(_lib, name), name
@@ -46,7 +47,7 @@ def test_header_enums_match_binding():
 
 def test_status_strings():
     lib = _lib.load()
-    for s in range(0, 10):
+    for s in range(0, 11):
         txt = lib.fa_status_str(s)
         assert txt and txt.decode() != "unknown status"
     assert lib.fa_status_str(99).decode() == "unknown status"
@@ -109,6 +110,35 @@ def test_check_order_is_stable():
     assert call(d=3, B=0) == _lib.FA_ERR_HEADDIM
 
 
+def call_ex(path, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return fa.fa_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                        a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], path, a["stream"])
+
+
+@pytest.mark.parametrize("path,kw", [
+    (3, {}),
+    (-1, {}),
+    (_lib.FA_PATH_SHORT, dict(Nk=1025, d=64)),      # 17 key tiles
+    (_lib.FA_PATH_SHORT, dict(Nk=1025, d=32)),
+    (_lib.FA_PATH_SHORT, dict(Nk=577, d=128)),      # 10 key tiles
+])
+def test_path_rejected_before_launch(path, kw):
+    assert call_ex(path, **kw) == _lib.FA_ERR_PATH
+
+
+def test_path_checked_after_the_other_arguments():
+    assert call_ex(7, q=0) == _lib.FA_ERR_NULLPTR
+    assert call_ex(7, d=48) == _lib.FA_ERR_HEADDIM
+    assert call_ex(7, o=Q) == _lib.FA_ERR_ALIAS
+    # the short path's key limit is reached exactly at 16 (d <= 64) and 9 (d = 128) tiles:
+    # those sizes pass the path check and fail only on the fake pointers' later checks
+    for path in (_lib.FA_PATH_AUTO, _lib.FA_PATH_TILED, _lib.FA_PATH_SHORT):
+        assert call_ex(path, Nk=1024, d=64, q=0) == _lib.FA_ERR_NULLPTR
+        assert call_ex(path, Nk=576, d=128, causal=5) == _lib.FA_ERR_CAUSAL
+
+
 def test_python_wrapper_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(1, 1, 4, 64, dtype=torch.float16)
@@ -120,3 +150,5 @@ def test_ctypes_signature():
     lib = _lib.load()
     assert lib.fa_fwd.restype is ctypes.c_int
     assert len(lib.fa_fwd.argtypes) == 14
+    assert lib.fa_fwd_ex.restype is ctypes.c_int
+    assert len(lib.fa_fwd_ex.argtypes) == 15

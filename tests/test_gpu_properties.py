@@ -95,3 +95,39 @@ def test_output_only_written_in_bounds():
     torch.cuda.synchronize()
     assert torch.all(big[:2048] == 7.0) and torch.all(big[2048 + n_o:] == 7.0)
     assert torch.all(lbig[:64] == 5.0) and torch.all(lbig[64 + B * H * N:] == 5.0)
+
+
+def test_graph_replay_matches_eager():
+    """Calls captured in a HIP graph give the eager result on every replay,
+    with eager work and synchronisation between the replays (both paths)."""
+    require_gpu()
+    note("graph replay")
+    import torch
+
+    import exact_attention_23_amd as fa
+
+    dev = torch.device("cuda:0")
+    for path, (Nq, Nk) in (("short", (200, 300)), ("tiled", (300, 500))):
+        q, k, v = (t.to(dev) for t in rand_inputs(2, 2, Nq, Nk, 64, "fp16", seed=Nk))
+        o = torch.empty_like(q)
+        lse = torch.empty((2, 2, Nq), dtype=torch.float32, device=dev)
+        o_ref, lse_ref = fa.attention(q, k, v, causal=True, path=path)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fa.attention(q, k, v, causal=True, out=o, lse=lse, path=path)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(3):
+                fa.attention(q, k, v, causal=True, out=o, lse=lse, path=path)
+        for rep in range(4):
+            o.zero_()
+            lse.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(o, o_ref), f"{path}: replay {rep} output differs"
+            assert torch.equal(lse, lse_ref), f"{path}: replay {rep} LSE differs"
+            fa.attention(q, k, v, causal=False, path=path)  # eager work between replays

@@ -44,16 +44,36 @@ SMALL = [
 ]
 
 
+def short_path_fits(Nk, d):
+    return (Nk + 63) // 64 <= (9 if d == 128 else 16)
+
+
+@pytest.mark.parametrize("path", ["tiled", "short"])
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%dH%d_q%dk%d_d%d_%s_%s" % (
     c[0], c[1], c[2], c[3], c[4], c[5], "causal" if c[6] else "full"))
-def test_small_shapes(case):
+def test_small_shapes(case, path):
+    """Each shape through both kernels, whichever the automatic choice is."""
     require_gpu()
     B, H, Nq, Nk, d, dt, causal = case
-    note(f"parity small {case}")
+    if path == "short" and not short_path_fits(Nk, d):
+        pytest.skip("key range beyond the short path")
+    note(f"parity small {case} path={path}")
     q, k, v = rand_inputs(B, H, Nq, Nk, d, dt, seed=Nq * 1000 + Nk + d)
-    o, lse = run_gpu(q, k, v, causal)
+    o, lse = run_gpu(q, k, v, causal, path=path)
     O, L = oracle.attention(q, k, v, scale=default_scale(d), causal=causal)
-    compare(o, lse, O, L, what=str(case))
+    compare(o, lse, O, L, what=f"{case} {path}")
+
+
+@pytest.mark.parametrize("d,Nk", [(32, 1024), (64, 1024), (128, 576), (128, 512)])
+def test_short_path_at_its_key_limit(d, Nk):
+    """The short path at its largest key range (16 or 9 waves per workgroup)."""
+    require_gpu()
+    note(f"parity short path limit d={d} Nk={Nk}")
+    for dt, causal in (("fp16", False), ("bf16", True)):
+        q, k, v = rand_inputs(1, 2, 70, Nk, d, dt, seed=d + Nk)
+        o, lse = run_gpu(q, k, v, causal, path="short")
+        O, L = oracle.attention(q, k, v, scale=default_scale(d), causal=causal)
+        compare(o, lse, O, L, what=f"short limit d={d} Nk={Nk} {dt} causal={causal}")
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.125, 0.5, 1e-3, 2.0])
@@ -62,9 +82,10 @@ def test_scales(scale):
     note(f"parity scale {scale}")
     q, k, v = rand_inputs(2, 2, 150, 150, 64, "fp16", seed=77)
     for causal in (False, True):
-        o, lse = run_gpu(q, k, v, causal, scale=scale)
         O, L = oracle.attention(q, k, v, scale=scale, causal=causal)
-        compare(o, lse, O, L, what=f"scale={scale} causal={causal}")
+        for path in ("tiled", "short"):
+            o, lse = run_gpu(q, k, v, causal, scale=scale, path=path)
+            compare(o, lse, O, L, what=f"scale={scale} causal={causal} {path}")
 
 
 def test_lse_null():
@@ -84,9 +105,10 @@ def test_large_logits_tail():
     for d in (32, 64, 128):
         q, k, v = rand_inputs(2, 2, 361, 361, d, "fp16", seed=d, sigma_qk=8.0, v_uniform=True)
         for causal in (False, True):
-            o, lse = run_gpu(q, k, v, causal)
             O, L = oracle.attention(q, k, v, scale=default_scale(d), causal=causal)
-            compare(o, lse, O, L, what=f"large logits d={d} causal={causal}")
+            for path in ("tiled", "short"):
+                o, lse = run_gpu(q, k, v, causal, path=path)
+                compare(o, lse, O, L, what=f"large logits d={d} causal={causal} {path}")
 
 
 @pytest.mark.parametrize("d", [32, 64, 128])
@@ -105,9 +127,10 @@ def test_reference_raised_midway(d, dtype):
         k[:, :, pos, :] = height
     k = k.to(q.dtype)
     for causal in (False, True):
-        o, lse = run_gpu(q, k, v, causal)
         O, L = oracle.attention(q, k, v, scale=default_scale(d), causal=causal)
-        compare(o, lse, O, L, what=f"raised reference d={d} {dtype} causal={causal}")
+        for path in ("tiled", "short"):
+            o, lse = run_gpu(q, k, v, causal, path=path)
+            compare(o, lse, O, L, what=f"raised reference d={d} {dtype} causal={causal} {path}")
 
 
 def test_rising_scores():
