@@ -4,9 +4,12 @@ TEST INFRASTRUCTURE ONLY. Nothing on the product path imports this package:
 only the tests, the smoke check and the benchmark's CPU-baseline leg may use
 it. It shares no code with the HIP kernels or their C-ABI.
 
-Every function here is pinned by tests/test_oracle.py (brute force on tiny
-inputs, closed forms, hand-derived fixtures under tests/golden/, invariants of
-the definition, and the CPU float64 scaled_dot_product_attention of PyTorch).
+Every function here is pinned: the forward (definition.py) by
+tests/test_oracle.py (brute force on tiny inputs, closed forms, hand-derived
+fixtures under tests/golden/, invariants of the definition, and the CPU
+float64 scaled_dot_product_attention of PyTorch), the gradients (backward.py)
+by tests/test_oracle_backward.py (central finite differences of the forward,
+float64 autograd of a plain PyTorch attention, closed forms and invariants).
 No function is "parity unpinned".
 """
 from .definition import (  # noqa: F401
@@ -18,4 +21,9 @@ from .definition import (  # noqa: F401
     attention_head,
     attention,
     attention_rows,
+)
+from .backward import (  # noqa: F401
+    attention_backward_head,
+    attention_backward,
+    row_delta,
 )
