@@ -1,4 +1,4 @@
-"""MI355X (gfx950) exact-attention forward: Python binding of libfa.so.
+"""MI355X (gfx950) exact attention, forward and backward: Python binding of libfa.so.
 
 The binding only marshals arguments; every step of the computation runs in
 the HIP kernels behind the C ABI declared in include/fa.h. PyTorch supplies
@@ -14,14 +14,15 @@ from . import _lib
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_FP16, FA_OK, FA_PATH_AUTO,  # noqa: F401
                    FA_PATH_SHORT, FA_PATH_TILED)
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_ex", "attention", "version"]
+__all__ = ["FaError", "fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_bytes", "attention",
+           "attention_backward", "flash_attention", "version"]
 
 _PATHS = {"auto": FA_PATH_AUTO, "tiled": FA_PATH_TILED, "short": FA_PATH_SHORT}
 
 
 class FaError(RuntimeError):
     def __init__(self, status: int, msg: str):
-        super().__init__(f"fa_fwd failed with status {status}: {msg}")
+        super().__init__(f"libfa call failed with status {status}: {msg}")
         self.status = status
 
 
@@ -46,6 +47,22 @@ def fa_fwd_ex(q: int, k: int, v: int, o: int, lse: Optional[int], B: int, H: int
     """fa_fwd with an explicit kernel choice (FA_PATH_*); returns the status."""
     return _lib.load().fa_fwd_ex(q, k, v, o, lse or None, B, H, Nq, Nk, d, float(scale),
                                  int(causal), int(dtype), int(path), stream or None)
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, Nq: int) -> int:
+    """Workspace bytes fa_bwd needs (-1 for invalid sizes)."""
+    return _lib.load().fa_bwd_workspace_bytes(B, H, Nq)
+
+
+def fa_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int,
+           workspace: int, workspace_bytes: int, B: int, H: int, Nq: int, Nk: int, d: int,
+           scale: float, causal: int, dtype: int, stream: int) -> int:
+    """Direct call of the backward C entry point with raw device addresses;
+    returns the status."""
+    return _lib.load().fa_bwd(q or None, k or None, v or None, o or None, dout or None,
+                              lse or None, dq or None, dk or None, dv or None,
+                              workspace or None, workspace_bytes, B, H, Nq, Nk, d,
+                              float(scale), int(causal), int(dtype), stream or None)
 
 
 def _current_stream(device_index: int):
@@ -123,9 +140,116 @@ def attention(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
     else:
         with torch.cuda.device(q.device):
             st = lib.fa_fwd_ex(*call, _current_stream(idx))
+    _check(st)
+    return out, lse
+
+
+def _check(st: int):
     if st != FA_OK:
         msg = status_str(st)
         if st == _lib.FA_ERR_LAUNCH:
             msg += ": " + _lib.load().fa_last_launch_error().decode()
         raise FaError(st, msg)
-    return out, lse
+
+
+def _check_gpu_4d(**tensors):
+    import torch
+
+    for name, t in tensors.items():
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+
+
+def attention_backward(q, k, v, out, dout, lse, *, causal: bool = False,
+                       scale: Optional[float] = None, dq=None, dk=None, dv=None):
+    """Gradients (dq, dk, dv) of attention for upstream gradient dout.
+
+    q, k, v, causal and scale are those of the forward call; out and lse are
+    its results (lse [B, H, Nq] float32). dout is shaped like q. All tensors
+    are contiguous GPU tensors on one device, q/k/v/out/dout in one fp16 or
+    bf16 dtype. Gradients come back in that dtype; dq/dk/dv may be passed to
+    write into existing tensors. The workspace is allocated here (torch's
+    caching allocator) and released when the call returns; the kernels run on
+    the current stream, which keeps it alive until they finish.
+    """
+    import torch
+
+    _check_gpu_4d(q=q, k=k, v=v, out=out, dout=dout)
+    if not (q.device == k.device == v.device == out.device == dout.device == lse.device):
+        raise ValueError("all tensors must be on one device")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
+        raise ValueError("q, k, v, out, dout must share a dtype")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
+        raise ValueError("k and v must be [B, H, Nk, d] matching q")
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must be shaped like q")
+    if (tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    grads = []
+    for name, g, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if g is None:
+            g = torch.empty_like(like)
+        elif (g.shape != like.shape or g.dtype != like.dtype or g.device != like.device
+              or not g.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous tensor like {'q' if name == 'dq' else name[1]}")
+        grads.append(g)
+    dq, dk, dv = grads
+    lib = _lib.load()
+    ws_bytes = lib.fa_bwd_workspace_bytes(B, H, Nq)
+    if ws_bytes < 0:
+        raise ValueError("sizes out of range for the backward pass")
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws_bytes,
+            B, H, Nq, Nk, d, float(scale), 1 if causal else 0, code)
+    idx = q.device.index
+    if idx == torch.cuda.current_device():
+        st = lib.fa_bwd(*call, _current_stream(idx))
+    else:
+        with torch.cuda.device(q.device):
+            st = lib.fa_bwd(*call, _current_stream(idx))
+    _check(st)
+    return dq, dk, dv
+
+
+def _autograd_function():
+    import torch
+
+    class FlashAttention(torch.autograd.Function):
+        """Forward through fa_fwd (keeping O and LSE), backward through fa_bwd."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, causal, scale):
+            q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+            o, lse = attention(q, k, v, causal=causal, scale=scale)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.causal, ctx.scale = causal, scale
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, o, lse = ctx.saved_tensors
+            dq, dk, dv = attention_backward(q, k, v, o, do.contiguous(), lse,
+                                            causal=ctx.causal, scale=ctx.scale)
+            return dq, dk, dv, None, None
+
+    return FlashAttention
+
+
+_FLASH_FN = None
+
+
+def flash_attention(q, k, v, *, causal: bool = False, scale: Optional[float] = None):
+    """Differentiable attention: O = softmax(scale * Q K^T [causal]) V, with
+    the gradients of Q, K and V computed by the backward kernels."""
+    global _FLASH_FN
+    if _FLASH_FN is None:
+        _FLASH_FN = _autograd_function()
+    return _FLASH_FN.apply(q, k, v, causal, scale)

@@ -17,6 +17,7 @@ FA_ERR_ALIGN = 7
 FA_ERR_ALIAS = 8
 FA_ERR_LAUNCH = 9
 FA_ERR_PATH = 10
+FA_ERR_WORKSPACE = 11
 
 FA_PATH_AUTO = 0
 FA_PATH_TILED = 1
@@ -56,6 +57,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                               ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     lib.fa_fwd_ex.restype = ctypes.c_int
+    lib.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.fa_bwd_workspace_bytes.restype = i64
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                           ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+    lib.fa_bwd.restype = ctypes.c_int
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_launch_error.argtypes = []

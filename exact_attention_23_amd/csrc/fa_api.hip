@@ -1,5 +1,5 @@
-// fa_api.hip - the C ABI of libfa.so: argument checks, tile selection, grid
-// computation and the launch of the gfx950 attention kernels.
+// fa_api.hip - the forward entry points of libfa.so: argument checks, tile
+// selection, grid computation and the launch of the gfx950 forward kernels.
 //
 // The declarations and the contract live in include/fa.h.
 #include <hip/hip_runtime.h>
@@ -8,12 +8,11 @@
 #include <stdint.h>
 
 #include "../../include/fa.h"
+#include "fa_host.hpp"
 #include "fa_fwd_kernel.hpp"
 #include "fa_fwd_short.hpp"
 
 namespace {
-
-constexpr int kVersion = 100;  // 0.1.0
 
 typedef void (*KernelFn)(fa::Params);
 
@@ -77,47 +76,9 @@ ShortVariant<T> pick_short(int64_t d, bool causal) {
   }
 }
 
-// Compute units of the current device (the tiled path fills them only
-// with at least this many workgroups).
-int device_cus() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 256;
-  return n > 0 ? n : 256;
-}
-
-// HIP's description of the last failed launch on this thread.
-thread_local const char* g_launch_error = "";
-
-bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
-  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
-  return a0 < b0 + bn && b0 < a0 + an;
-}
-
 }  // namespace
 
 extern "C" {
-
-int fa_version(void) { return kVersion; }
-
-const char* fa_last_launch_error(void) { return g_launch_error; }
-
-const char* fa_status_str(int status) {
-  switch (status) {
-    case FA_OK: return "ok";
-    case FA_ERR_NULLPTR: return "q, k, v or o is a null pointer";
-    case FA_ERR_SHAPE: return "B, H, Nq and Nk must be >= 1 and Nq*d, Nk*d < 2^29";
-    case FA_ERR_HEADDIM: return "head width d must be 32, 64 or 128";
-    case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16";
-    case FA_ERR_SCALE: return "scale must be finite";
-    case FA_ERR_CAUSAL: return "causal must be 0 or 1";
-    case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
-    case FA_ERR_ALIAS: return "o or lse overlaps an input or each other";
-    case FA_ERR_LAUNCH: return "kernel launch failed";
-    case FA_ERR_PATH: return "unknown path, or the short path with too many keys for it";
-    default: return "unknown status";
-  }
-}
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
@@ -154,12 +115,12 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
   const size_t qo_bytes = (size_t)(B * H) * (size_t)(Nq * d) * es;
   const size_t kv_bytes = (size_t)(B * H) * (size_t)(Nk * d) * es;
   const size_t lse_bytes = (size_t)(B * H) * (size_t)Nq * 4;
-  if (overlaps(o, qo_bytes, q, qo_bytes) || overlaps(o, qo_bytes, k, kv_bytes) ||
-      overlaps(o, qo_bytes, v, kv_bytes))
+  if (fa::overlaps(o, qo_bytes, q, qo_bytes) || fa::overlaps(o, qo_bytes, k, kv_bytes) ||
+      fa::overlaps(o, qo_bytes, v, kv_bytes))
     return FA_ERR_ALIAS;
   if (lse != nullptr &&
-      (overlaps(lse, lse_bytes, q, qo_bytes) || overlaps(lse, lse_bytes, k, kv_bytes) ||
-       overlaps(lse, lse_bytes, v, kv_bytes) || overlaps(lse, lse_bytes, o, qo_bytes)))
+      (fa::overlaps(lse, lse_bytes, q, qo_bytes) || fa::overlaps(lse, lse_bytes, k, kv_bytes) ||
+       fa::overlaps(lse, lse_bytes, v, kv_bytes) || fa::overlaps(lse, lse_bytes, o, qo_bytes)))
     return FA_ERR_ALIAS;
   if (path != FA_PATH_AUTO && path != FA_PATH_TILED && path != FA_PATH_SHORT) return FA_ERR_PATH;
   const int64_t key_tiles = (Nk + 63) / 64;
@@ -171,7 +132,7 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
   // Latency-bound sizes: the short path's workgroups (one per 32 rows, at
   // most one per compute unit for its LDS) all run at once.
   const bool use_short =
-      path == FA_PATH_SHORT || (path == FA_PATH_AUTO && short_fits && short_total <= device_cus());
+      path == FA_PATH_SHORT || (path == FA_PATH_AUTO && short_fits && short_total <= fa::device_cus());
 
   fa::Params p;
   p.q = q;
@@ -212,12 +173,7 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
     e = hipLaunchKernel((const void*)var.fn, dim3((unsigned)total), dim3(var.threads), args, 0,
                         (hipStream_t)stream);
   }
-  if (e == hipSuccess) e = hipGetLastError();
-  if (e != hipSuccess) {
-    g_launch_error = hipGetErrorString(e);
-    return FA_ERR_LAUNCH;
-  }
-  return FA_OK;
+  return fa::launch_status(e);
 }
 
 }  // extern "C"

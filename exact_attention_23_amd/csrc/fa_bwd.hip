@@ -1,0 +1,164 @@
+// fa_bwd.hip - the backward entry points of libfa.so: argument checks, grid
+// computation and the launch of the three gfx950 backward kernels.
+//
+// The declarations and the contract live in include/fa.h.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_bwd_kernel.hpp"
+#include "fa_host.hpp"
+
+namespace {
+
+typedef void (*BwdFn)(fa::BwdParams);
+
+struct BwdKernels {
+  BwdFn pre, dkdv, dq;
+  int pre_rows;      // query rows per workgroup of the D/LSE kernel
+  int dkdv_threads;  // threads per dK/dV workgroup
+  int dkdv_bn;       // keys per dK/dV workgroup
+  int dq_threads;    // threads per dQ workgroup
+  int dq_bm;         // query rows per dQ workgroup
+};
+
+// Waves per workgroup and ring stages: both kernels run 4 waves of 32 keys
+// (dK/dV) or 32 query rows (dQ). At d = 128 their operand and accumulator
+// registers leave one wave per SIMD, and the dQ ring has 3 stages to fit LDS.
+template <int D, bool C, typename T>
+BwdKernels make_bwd() {
+  constexpr int NWA = 4, SA = 3;
+  constexpr int NWB = 4;
+  constexpr int SB = D == 128 ? 3 : 4;
+  return {fa::fa_bwd_pre_kernel<D, T>,
+          fa::fa_bwd_dkdv_kernel<D, NWA, SA, C, T>,
+          fa::fa_bwd_dq_kernel<D, NWB, SB, C, T>,
+          256 / (D / 8),
+          64 * NWA,
+          32 * NWA,
+          64 * NWB,
+          32 * NWB};
+}
+
+template <typename T>
+BwdKernels pick_bwd(int64_t d, bool causal) {
+  switch (d) {
+    case 32: return causal ? make_bwd<32, true, T>() : make_bwd<32, false, T>();
+    case 64: return causal ? make_bwd<64, true, T>() : make_bwd<64, false, T>();
+    default: return causal ? make_bwd<128, true, T>() : make_bwd<128, false, T>();
+  }
+}
+
+hipError_t launch(BwdFn fn, int64_t grid, int threads, fa::BwdParams& p, hipStream_t stream) {
+  void* args[] = {&p};
+  return hipLaunchKernel((const void*)fn, dim3((unsigned)grid), dim3((unsigned)threads), args, 0, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq) {
+  if (B < 1 || H < 1 || Nq < 1) return -1;
+  const int64_t lim = (int64_t)1 << 31;
+  if (B >= lim || H >= lim || B * H >= lim || Nq > ((int64_t)1 << 29)) return -1;
+  return B * H * ((Nq + 31) / 32) * 256;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace,
+           int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+           float scale, int causal, int dtype, void* stream) {
+  // ---- every check happens before the first HIP call
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr ||
+      lse == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+    return FA_ERR_NULLPTR;
+  if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (d != 32 && d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t head_lim = (int64_t)1 << 29;
+  if (Nq > head_lim || Nk > head_lim || Nq * d >= head_lim || Nk * d >= head_lim) return FA_ERR_SHAPE;
+  if (B > lim || H > lim || B * H >= lim) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
+       (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u)
+    return FA_ERR_ALIGN;
+  if (((uintptr_t)lse) & 3u) return FA_ERR_ALIGN;
+  const int64_t ws_need = fa_bwd_workspace_bytes(B, H, Nq);
+  if (workspace == nullptr || ((uintptr_t)workspace & 15u) || ws_need < 0 || workspace_bytes < ws_need)
+    return FA_ERR_WORKSPACE;
+
+  const BwdKernels ker = dtype == FA_DTYPE_FP16 ? pick_bwd<_Float16>(d, causal != 0)
+                                                : pick_bwd<__bf16>(d, causal != 0);
+  const int64_t nrec = (Nq + 31) / 32;
+  const int64_t pre_grid = (B * H * nrec * 32 + ker.pre_rows - 1) / ker.pre_rows;
+  const int64_t nkb = (Nk + ker.dkdv_bn - 1) / ker.dkdv_bn;
+  const int64_t nqb = (Nq + ker.dq_bm - 1) / ker.dq_bm;
+  const int64_t dkdv_grid = B * H * nkb;
+  const int64_t dq_grid = B * H * nqb;
+  if (pre_grid >= lim || dkdv_grid >= lim || dq_grid >= lim) return FA_ERR_SHAPE;
+
+  // Outputs and the workspace are written: none may overlap an input, and
+  // they may not overlap each other.
+  const size_t q_bytes = (size_t)(B * H) * (size_t)(Nq * d) * 2;
+  const size_t kv_bytes = (size_t)(B * H) * (size_t)(Nk * d) * 2;
+  const size_t lse_bytes = (size_t)(B * H) * (size_t)Nq * 4;
+  struct Range {
+    const void* p;
+    size_t n;
+  };
+  const Range inputs[] = {{q, q_bytes}, {k, kv_bytes}, {v, kv_bytes}, {o, q_bytes},
+                          {dout, q_bytes}, {lse, lse_bytes}};
+  const Range written[] = {{dq, q_bytes}, {dk, kv_bytes}, {dv, kv_bytes},
+                           {workspace, (size_t)ws_need}};
+  for (const Range& w : written) {
+    for (const Range& in : inputs)
+      if (fa::overlaps(w.p, w.n, in.p, in.n)) return FA_ERR_ALIAS;
+    for (const Range& w2 : written)
+      if (&w2 != &w && fa::overlaps(w.p, w.n, w2.p, w2.n)) return FA_ERR_ALIAS;
+  }
+
+  fa::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.aux = (float*)workspace;
+  p.B = (int)B;
+  p.H = (int)H;
+  p.Nq = (int)Nq;
+  p.Nk = (int)Nk;
+  p.nrec = (int)nrec;
+  p.group = 1;
+  p.c = scale * fa::kLog2e;
+  p.scale = scale;
+  hipStream_t st = (hipStream_t)stream;
+
+  p.nblk = 0;
+  p.xcd_q = p.xcd_r = 0;
+  hipError_t e = launch(ker.pre, pre_grid, 256, p, st);
+  if (e != hipSuccess) return fa::launch_status(e);
+
+  p.nblk = (int)nkb;
+  p.xcd_q = fa::xcd_split(dkdv_grid).q;
+  p.xcd_r = fa::xcd_split(dkdv_grid).r;
+  e = launch(ker.dkdv, dkdv_grid, ker.dkdv_threads, p, st);
+  if (e != hipSuccess) return fa::launch_status(e);
+
+  p.nblk = (int)nqb;
+  p.xcd_q = fa::xcd_split(dq_grid).q;
+  p.xcd_r = fa::xcd_split(dq_grid).r;
+  e = launch(ker.dq, dq_grid, ker.dq_threads, p, st);
+  return fa::launch_status(e);
+}
+
+}  // extern "C"

@@ -1,7 +1,7 @@
 /*
- * fa.h - C ABI of the MI355X (gfx950) exact-attention forward library, libfa.so.
+ * fa.h - C ABI of the MI355X (gfx950) exact-attention library, libfa.so.
  *
- * Operation (the only one on the path): for every batch b and head h,
+ * Forward operation: for every batch b and head h,
  *
  *     S   = scale * Q K^T                    (Nq x Nk)
  *     S_ij = -inf where causal and j > i     (top-left aligned)
@@ -43,17 +43,20 @@ extern "C" {
 /* Status codes returned by fa_fwd. */
 enum fa_status {
   FA_OK = 0,
-  FA_ERR_NULLPTR = 1, /* q, k, v or o is NULL                                    */
+  FA_ERR_NULLPTR = 1, /* a tensor argument is NULL (lse may be NULL in fa_fwd)   */
   FA_ERR_SHAPE = 2,   /* B, H, Nq or Nk < 1, or an index product too large     */
   FA_ERR_HEADDIM = 3, /* d not in {32, 64, 128}                                 */
   FA_ERR_DTYPE = 4,   /* dtype not FA_DTYPE_FP16 or FA_DTYPE_BF16               */
   FA_ERR_SCALE = 5,   /* scale is NaN or infinite                               */
   FA_ERR_CAUSAL = 6,  /* causal not 0 or 1                                      */
-  FA_ERR_ALIGN = 7,   /* q, k, v, o not 16-byte aligned, or lse not 4-byte      */
-  FA_ERR_ALIAS = 8,   /* o or lse overlaps an input, or o overlaps lse          */
+  FA_ERR_ALIGN = 7,   /* a tensor not 16-byte aligned, or lse not 4-byte        */
+  FA_ERR_ALIAS = 8,   /* an output overlaps an input, another output or the     */
+                      /* workspace                                              */
   FA_ERR_LAUNCH = 9,  /* the kernel launch itself failed (hipGetLastError)      */
-  FA_ERR_PATH = 10    /* fa_fwd_ex: unknown path, or FA_PATH_SHORT with Nk too  */
+  FA_ERR_PATH = 10,   /* fa_fwd_ex: unknown path, or FA_PATH_SHORT with Nk too  */
                       /* large for it                                           */
+  FA_ERR_WORKSPACE = 11 /* fa_bwd: workspace NULL, not 16-byte aligned, or      */
+                        /* smaller than fa_bwd_workspace_bytes                  */
 };
 
 /* Element types of q, k, v and o (all four share one type). Accumulation is
@@ -118,6 +121,66 @@ enum fa_path { FA_PATH_AUTO = 0, FA_PATH_TILED = 1, FA_PATH_SHORT = 2 };
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
               float scale, int causal, int dtype, int path, void* stream);
+
+/*
+ * Backward pass. For an upstream gradient dO of the forward's output O, the
+ * gradients of the scalar sum(O * dO) with respect to Q, K and V, per (b, h):
+ *
+ *     P   = softmax_rows(scale * Q K^T [causal mask])   recomputed from LSE
+ *     dV  = P^T dO
+ *     dP  = dO V^T
+ *     D_i = sum_c dO_ic O_ic         (= sum_j P_ij dP_ij)
+ *     dS  = P * (dP - D)             (elementwise, D broadcast along rows)
+ *     dQ  = scale * dS K
+ *     dK  = scale * dS^T Q
+ *
+ * The pages state that training keeps the forward's softmax statistics for
+ * the backward pass (kwkr.cn YOLO11 FlashAttention-2 article, section 2.3) and
+ * that the backward recomputes the attention weights rather than storing them
+ * ("YOLOv12推理速度翻倍秘诀：Flash Attention加持", section 1); the formulas are the
+ * chain rule of the forward definition above. P is rebuilt tile by tile from
+ * Q, K and the forward's LSE as P = exp(scale * q.k - LSE), so no Nq x Nk
+ * matrix reaches device memory here either.
+ */
+
+/*
+ * fa_bwd_workspace_bytes - bytes of device workspace fa_bwd needs for B*H
+ * heads of Nq query rows: 256 * B * H * ceil(Nq / 32) (two fp32 values per
+ * query row, rows padded to a multiple of 32). Returns -1 when B, H or Nq is
+ * below 1 or the size does not fit in int64_t.
+ */
+int64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq);
+
+/*
+ * fa_bwd - gradients dQ, dK, dV of exact attention.
+ *
+ *   q, k, v    the forward's inputs, layouts and dtype as in fa_fwd
+ *   o          [B, H, Nq, d] the forward's output O for these inputs
+ *   dout       [B, H, Nq, d] upstream gradient dO, same dtype
+ *   lse        [B, H, Nq] fp32, the forward's LSE (natural log) for the same
+ *              q, k, scale and causal; the weights are rebuilt from it, so an
+ *              LSE from other inputs gives meaningless gradients
+ *   dq         [B, H, Nq, d] output, dtype of q
+ *   dk, dv     [B, H, Nk, d] outputs, dtype of q
+ *   workspace  device memory of at least fa_bwd_workspace_bytes(B, H, Nq)
+ *              bytes, 16-byte aligned, owned by the caller; its contents on
+ *              entry do not matter and are overwritten. It must not overlap
+ *              any tensor argument.
+ *   workspace_bytes  its size in bytes
+ *   B, H, Nq, Nk, d, scale, causal, dtype, stream: as in fa_fwd
+ *
+ * dq, dk and dv must not overlap each other, any input or the workspace.
+ * Work is enqueued on `stream` as three kernels (per-row D and the scaled
+ * LSE into the workspace; dK and dV per block of keys; dQ per block of
+ * query rows), so the workspace must stay allocated until they have run.
+ * Returns FA_OK once enqueued, otherwise an fa_status code (all checks are
+ * made before any HIP call). Accumulation is fp32; every output element is
+ * summed in a fixed order, so results are deterministic (no atomics).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace,
+           int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+           float scale, int causal, int dtype, void* stream);
 
 /* A static, human-readable description of a status code (never NULL). */
 const char* fa_status_str(int status);

@@ -1,7 +1,7 @@
 """The C ABI of libfa.so, checked without a GPU.
 
-Every argument check in fa_fwd runs before any HIP call, so invalid calls can
-be made here; no valid (launching) call is made.
+Every argument check in fa_fwd and fa_bwd runs before any HIP call, so
+invalid calls can be made here; no valid (launching) call is made.
 """
 import ctypes
 import os
@@ -39,7 +39,7 @@ def test_header_enums_match_binding():
     for name in ["FA_OK", "FA_ERR_NULLPTR", "FA_ERR_SHAPE", "FA_ERR_HEADDIM", "FA_ERR_DTYPE",
                  "FA_ERR_SCALE", "FA_ERR_CAUSAL", "FA_ERR_ALIGN", "FA_ERR_ALIAS", "FA_ERR_LAUNCH",
                  "FA_ERR_PATH", "FA_DTYPE_FP16", "FA_DTYPE_BF16", "FA_PATH_AUTO", "FA_PATH_TILED",
-                 "FA_PATH_SHORT"]:
+                 "FA_PATH_SHORT", "FA_ERR_WORKSPACE"]:
         m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
         assert m, name
         assert int(m.group(1)) == getattr(_lib, name), name
@@ -47,7 +47,7 @@ def test_header_enums_match_binding():
 
 def test_status_strings():
     lib = _lib.load()
-    for s in range(0, 11):
+    for s in range(0, 12):
         txt = lib.fa_status_str(s)
         assert txt and txt.decode() != "unknown status"
     assert lib.fa_status_str(99).decode() == "unknown status"
@@ -152,3 +152,69 @@ def test_ctypes_signature():
     assert len(lib.fa_fwd.argtypes) == 14
     assert lib.fa_fwd_ex.restype is ctypes.c_int
     assert len(lib.fa_fwd_ex.argtypes) == 15
+
+
+# ---- backward entry points
+DO, DQ, DK, DV, WS = 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0xA0000000
+BGOOD = dict(q=Q, k=K, v=V, o=O, dout=DO, lse=L, dq=DQ, dk=DK, dv=DV, ws=WS, ws_bytes=1 << 20,
+             B=2, H=3, Nq=100, Nk=77, d=64, scale=0.125, causal=0, dtype=0, stream=None)
+
+
+def bcall(**kw):
+    a = dict(BGOOD)
+    a.update(kw)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"],
+                     a["dv"], a["ws"], a["ws_bytes"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                     a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+def test_workspace_size():
+    # two fp32 values per query row, rows padded to 32
+    assert fa.fa_bwd_workspace_bytes(2, 3, 100) == 2 * 3 * 4 * 256
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1) == 256
+    assert fa.fa_bwd_workspace_bytes(1, 1, 32) == 256
+    assert fa.fa_bwd_workspace_bytes(1, 1, 33) == 512
+    assert fa.fa_bwd_workspace_bytes(0, 1, 1) == -1
+    assert fa.fa_bwd_workspace_bytes(1, 0, 1) == -1
+    assert fa.fa_bwd_workspace_bytes(1, 1, 0) == -1
+    assert fa.fa_bwd_workspace_bytes(1 << 20, 1 << 12, 1) == -1
+    assert fa.fa_bwd_workspace_bytes(1, 1, (1 << 29) + 1) == -1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), _lib.FA_ERR_NULLPTR),
+    (dict(o=0), _lib.FA_ERR_NULLPTR),
+    (dict(dout=0), _lib.FA_ERR_NULLPTR),
+    (dict(lse=0), _lib.FA_ERR_NULLPTR),
+    (dict(dq=0), _lib.FA_ERR_NULLPTR),
+    (dict(dk=0), _lib.FA_ERR_NULLPTR),
+    (dict(dv=0), _lib.FA_ERR_NULLPTR),
+    (dict(dtype=2), _lib.FA_ERR_DTYPE),
+    (dict(d=96), _lib.FA_ERR_HEADDIM),
+    (dict(Nk=0), _lib.FA_ERR_SHAPE),
+    (dict(Nq=(1 << 29) // 32, d=32), _lib.FA_ERR_SHAPE),
+    (dict(causal=3), _lib.FA_ERR_CAUSAL),
+    (dict(scale=float("nan")), _lib.FA_ERR_SCALE),
+    (dict(dout=DO + 8), _lib.FA_ERR_ALIGN),
+    (dict(dk=DK + 4), _lib.FA_ERR_ALIGN),
+    (dict(lse=L + 1), _lib.FA_ERR_ALIGN),
+    (dict(ws=0), _lib.FA_ERR_WORKSPACE),
+    (dict(ws=WS + 8), _lib.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=2 * 3 * 4 * 256 - 1), _lib.FA_ERR_WORKSPACE),
+    (dict(dq=Q), _lib.FA_ERR_ALIAS),
+    (dict(dk=V + 512), _lib.FA_ERR_ALIAS),
+    (dict(dv=DO), _lib.FA_ERR_ALIAS),
+    (dict(dv=DK + 256), _lib.FA_ERR_ALIAS),
+    (dict(ws=DQ + 1024), _lib.FA_ERR_ALIAS),
+    (dict(ws=L), _lib.FA_ERR_ALIAS),
+    (dict(dq=WS), _lib.FA_ERR_ALIAS),
+])
+def test_bwd_invalid_arguments_rejected_before_launch(kw, status):
+    assert bcall(**kw) == status
+
+
+def test_bwd_exact_workspace_is_enough_for_the_checks():
+    # a workspace of exactly fa_bwd_workspace_bytes passes its check; the call
+    # then fails a later check (an alias), so nothing is launched
+    need = fa.fa_bwd_workspace_bytes(2, 3, 100)
+    assert bcall(ws_bytes=need, dv=K) == _lib.FA_ERR_ALIAS

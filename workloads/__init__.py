@@ -109,6 +109,19 @@ def make_inputs(w: Workload, seed: Optional[int] = None):
     return q.contiguous(), k.contiguous(), v.contiguous()
 
 
+# Offset between a workload's input seed and the seed of its upstream gradient.
+GRAD_SEED_OFFSET = 500_000
+
+
+def make_grad(w: Workload, seed: Optional[int] = None) -> torch.Tensor:
+    """Draw the upstream gradient dO for the backward pass: [B,H,Nq,d] iid
+    N(0, 1) in float32 from its own torch CPU generator (seeded with
+    (seed or w.seed) + GRAD_SEED_OFFSET), rounded to w's storage dtype."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed((w.seed if seed is None else seed) + GRAD_SEED_OFFSET)
+    return _draw(g, (w.B, w.H, w.Nq, w.d), ("normal", 1.0)).to(w.torch_dtype).contiguous()
+
+
 def sha256(t: torch.Tensor) -> str:
     """sha256 of a CPU tensor's raw bytes (for recording which inputs ran)."""
     t = t.detach().cpu().contiguous()
