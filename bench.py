@@ -34,18 +34,23 @@ PEAK_MFMA_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_23_amd", "csrc", f)
-                  for f in ("fa_fwd_kernel.hpp", "fa_fwd_short.hpp", "fa_api.hip")]
+                  for f in ("fa_device.hpp", "fa_fwd_kernel.hpp", "fa_fwd_short.hpp", "fa_api.hip")]
+BWD_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_23_amd", "csrc", f)
+                      for f in ("fa_device.hpp", "fa_bwd_kernel.hpp", "fa_bwd.hip")]
+# backward kernels as rocprofv3 names them, and the FA_BWD_* bit of each
+BWD_KERNELS = (("pre", "fa_bwd_pre_kernel", 1), ("dkdv", "fa_bwd_dkdv_kernel", 2),
+               ("dq", "fa_bwd_dq_kernel", 4))
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (sources or KERNEL_SOURCES):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(key: str, sources=None):
     """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
     or None when absent or taken on a different kernel source."""
     try:
@@ -53,8 +58,8 @@ def measured_traffic(workload: str):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = rec.get("workloads", {}).get(workload)
-    if not ent or ent.get("kernel_source_sha") != kernel_source_hash():
+    ent = rec.get("workloads", {}).get(key)
+    if not ent or ent.get("kernel_source_sha") != kernel_source_hash(sources):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -137,6 +142,128 @@ def time_graph(w, calls: int = 100, replays: int = 20):
     return us
 
 
+class _Bwd:
+    """Device buffers and the raw fa_bwd_ex call for one workload: inputs, the
+    forward's O and LSE, an upstream gradient, gradients and workspace."""
+
+    def __init__(self, w):
+        import torch
+
+        import exact_attention_23_amd as fa
+        from workloads import make_grad, make_inputs
+
+        dev = torch.device("cuda:0")
+        self.w = w
+        self.q, self.k, self.v = (t.to(dev) for t in make_inputs(w))
+        self.do = make_grad(w).to(dev)
+        self.o, self.lse = fa.attention(self.q, self.k, self.v, causal=w.causal, scale=w.scale)
+        self.dq, self.dk, self.dv = (torch.empty_like(t) for t in (self.q, self.k, self.v))
+        self.lib = fa._lib.load()
+        nbytes = self.lib.fa_bwd_workspace_bytes(w.B, w.H, w.Nq)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.args = (self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr(),
+                     self.do.data_ptr(), self.lse.data_ptr(), self.dq.data_ptr(),
+                     self.dk.data_ptr(), self.dv.data_ptr(), self.ws.data_ptr(), nbytes,
+                     w.B, w.H, w.Nq, w.Nk, w.d, float(w.scale), 1 if w.causal else 0,
+                     fa._dtype_code(self.q))
+        self.stream = fa._current_stream(0)
+        self.fa = fa
+
+    def __call__(self, mask: int = 7):
+        st = self.lib.fa_bwd_ex(*self.args, mask, self.stream)
+        if st != 0:
+            raise RuntimeError(f"fa_bwd_ex failed: {self.fa.status_str(st)}")
+
+
+def time_bwd(w, steps: int, warmup: int, settle_ms: float = 300.0):
+    """Backward pass of w: ms per whole call (three kernels) and the average
+    duration of each kernel alone (HIP events around `steps` launches of that
+    kernel only, on the stream the library launches on)."""
+    import torch
+
+    b = _Bwd(w)
+    for _ in range(warmup):
+        b()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(4):
+            b()
+        torch.cuda.synchronize()
+
+    def timed(mask):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(steps):
+            b(mask)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / steps
+
+    ms = timed(7)
+    per = {name: timed(bit) for name, _, bit in BWD_KERNELS}
+    for t in (b.dq, b.dk, b.dv):
+        if not torch.isfinite(t.float()).all():
+            raise RuntimeError("non-finite gradient in the timed run")
+    return ms, per
+
+
+def bwd_record(w, ms: float, per: dict):
+    """Backward figures of w: whole-pass TFLOP/s over the five products of
+    the gradient definition (10*B*H*Nq*Nk*d, halved when causal) and the
+    roofline of the dominant kernel."""
+    flops_total = 2.5 * w.flops()
+    # products each kernel computes: dK/dV forms S, dP, dV, dK; dQ forms S
+    # and dP again and dQ (only dQ is new work); the D/LSE pass is bytes
+    dom = max(("dkdv", "dq"), key=lambda n: per[n])
+    dom_flops = {"dkdv": 2.0 * w.flops(), "dq": 1.5 * w.flops()}[dom]
+    achieved = dom_flops / (per[dom] * 1e-3) / 1e12
+    kname = dict((n, k) for n, k, _ in BWD_KERNELS)[dom]
+    tflops = flops_total / (ms * 1e-3) / 1e12
+    return {
+        "value": round(tflops, 3), "unit": "TFLOP/s", "ms_per_step": round(ms, 6),
+        "mfma_peak_frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
+        "kernels_us": {n: round(per[n] * 1e3, 3) for n in per},
+        "roofline": {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": measured_traffic(f"bwd:{w.name}", BWD_KERNEL_SOURCES)},
+        "kernel_source_sha": kernel_source_hash(BWD_KERNEL_SOURCES),
+    }
+
+
+def cpu_baseline_bwd(w, budget_s: float = 12.0):
+    """The gradient oracle on whole heads of w until ~budget_s of CPU time."""
+    import numpy as np
+
+    import oracle
+    from workloads import make_grad, make_inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    q, k, v = make_inputs(w)
+    do = make_grad(w)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    order = [heads[i] for i in np.random.default_rng(0).permutation(len(heads))]
+    done = 0
+    t0 = time.perf_counter()
+    for (b, h) in order:
+        oracle.attention_backward_head(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 2.5 * w.flops() * done / len(heads)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads (whole heads) of {w.name}, backward; "
+                      f"{dt:.1f} s wall; numpy float64"}
+
+
 def cpu_baseline(w, budget_s: float = 12.0):
     """The oracle on whole heads of w until ~budget_s of CPU time is spent."""
     import numpy as np
@@ -200,17 +327,19 @@ def _counter_rows(csv_dir: str, counter: str):
 
 
 def write_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str,
-                  copy_write_dir: str, copy_mib: int, command: str):
-    """Record HBM bytes per launch of the attention kernel from rocprofv3
-    FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch), each scaled by what the
-    same counter reads for a plain copy of copy_mib MiB (known bytes)."""
+                  copy_write_dir: str, copy_mib: int, command: str, bwd: bool = False):
+    """Record HBM bytes per launch of the attention kernel (the forward, or
+    with bwd the dK/dV kernel of the backward, keyed "bwd:<workload>") from
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch), each scaled by
+    what the same counter reads for a plain copy of copy_mib MiB (known bytes)."""
     import statistics
 
     known = copy_mib * (1 << 20)
     cf = [v for k, v in _counter_rows(copy_fetch_dir, "FETCH_SIZE") if "copyBuffer" in k or "copy" in k.lower()]
     cw = [v for k, v in _counter_rows(copy_write_dir, "WRITE_SIZE") if "copyBuffer" in k or "copy" in k.lower()]
-    kf = [v for k, v in _counter_rows(fetch_dir, "FETCH_SIZE") if "fa_fwd_kernel" in k]
-    kw = [v for k, v in _counter_rows(write_dir, "WRITE_SIZE") if "fa_fwd_kernel" in k]
+    kname = "fa_bwd_dkdv_kernel" if bwd else "fa_fwd_kernel"
+    kf = [v for k, v in _counter_rows(fetch_dir, "FETCH_SIZE") if kname in k]
+    kw = [v for k, v in _counter_rows(write_dir, "WRITE_SIZE") if kname in k]
     if not (cf and cw and kf and kw):
         raise RuntimeError("missing counter rows")
     f_scale = known / (statistics.median(cf) * 1024)
@@ -222,11 +351,14 @@ def write_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir:
             rec = json.load(fh)
     except (OSError, ValueError):
         rec = {}
-    rec.setdefault("about", "HBM bytes per launch of fa_fwd_kernel from rocprofv3 FETCH_SIZE and "
-                   "WRITE_SIZE (KiB per dispatch), scaled by the same counters on a plain "
-                   "device copy of known size. Written by bench.py --write-traffic.")
-    rec.setdefault("workloads", {})[workload] = {
-        "kernel_source_sha": kernel_source_hash(),
+    rec["about"] = ("HBM bytes per launch of fa_fwd_kernel (key: workload) and of "
+                    "fa_bwd_dkdv_kernel (key: bwd:workload) from rocprofv3 FETCH_SIZE and "
+                    "WRITE_SIZE (KiB per dispatch), scaled by the same counters on a plain "
+                    "device copy of known size. Written by bench.py --write-traffic.")
+    key = f"bwd:{workload}" if bwd else workload
+    rec.setdefault("workloads", {})[key] = {
+        "kernel": kname,
+        "kernel_source_sha": kernel_source_hash(BWD_KERNEL_SOURCES if bwd else None),
         "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
         "hbm_bytes_per_launch": round(fetch + write),
         "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
@@ -236,7 +368,7 @@ def write_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir:
     with open(TRAFFIC_FILE, "w", encoding="utf-8") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
-    return rec["workloads"][workload]
+    return rec["workloads"][key]
 
 
 def main(argv=None):
@@ -255,10 +387,15 @@ def main(argv=None):
                                                          "COPY_WRITE_DIR", "COPY_MIB"),
                     help="record HBM traffic of --workload from rocprofv3 --pmc CSV directories")
     ap.add_argument("--command", default="", help="profiling command recorded with --write-traffic")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="fwd (default): the forward line, with the backward of the same "
+                         "workload attached; bwd: a line for the backward pass alone")
+    ap.add_argument("--no-bwd", action="store_true", help="leave the backward out of the fwd line")
     args = ap.parse_args(argv)
     if args.write_traffic:
         fd, wd, cfd, cwd, mib = args.write_traffic
-        print(json.dumps(write_traffic(args.workload, fd, wd, cfd, cwd, int(mib), args.command)))
+        print(json.dumps(write_traffic(args.workload, fd, wd, cfd, cwd, int(mib), args.command,
+                                       bwd=args.which == "bwd")))
         return 0
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
@@ -272,6 +409,26 @@ def main(argv=None):
     from workloads import WORKLOADS
 
     w = WORKLOADS[args.workload]
+    if args.which == "bwd":
+        ms, per = time_bwd(w, args.steps, args.warmup, args.settle_ms)
+        rec = bwd_record(w, ms, per)
+        line = {
+            "metric": "attention bwd TFLOP/s (dQ, dK, dV; 10*B*H*Nq*Nk*d FLOP, halved when "
+                      "causal) and % MFMA peak",
+            "value": rec["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": rec["ms_per_step"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+            "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                       "causal": w.causal, "input_dtype": w.dtype, "accumulate": "fp32",
+                       "parallelism": "single GPU; grids over (batch, head, key block) and "
+                                      "(batch, head, query block)"},
+            "mfma_peak_frac": rec["mfma_peak_frac"], "kernels_us": rec["kernels_us"],
+            "roofline": rec["roofline"], "kernel_source_sha": rec["kernel_source_sha"],
+        }
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_bwd(w)
+        print(json.dumps(line), flush=True)
+        return 0
     ms = time_gpu(w, args.steps, args.warmup, args.settle_ms)
     tflops = w.flops() / (ms * 1e-3) / 1e12
     n400_us = n400_eager_us = None
@@ -309,6 +466,11 @@ def main(argv=None):
         "algorithmic_hbm_gbs": round(w.algorithmic_bytes() / (ms * 1e-3) / 1e9, 1),
         "kernel_source_sha": kernel_source_hash(),
     }
+    if not args.no_bwd:
+        # the backward pass of the same workload (a separate figure: the
+        # headline value above is the forward's)
+        bms, bper = time_bwd(w, max(args.steps // 2, 5), max(args.warmup // 2, 2), args.settle_ms)
+        line["backward"] = bwd_record(w, bms, bper)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

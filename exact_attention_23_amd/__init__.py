@@ -14,7 +14,7 @@ from . import _lib
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_FP16, FA_OK, FA_PATH_AUTO,  # noqa: F401
                    FA_PATH_SHORT, FA_PATH_TILED)
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_workspace_bytes", "attention",
+__all__ = ["FaError", "fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_bytes", "attention",
            "attention_backward", "flash_attention", "version"]
 
 _PATHS = {"auto": FA_PATH_AUTO, "tiled": FA_PATH_TILED, "short": FA_PATH_SHORT}
@@ -63,6 +63,16 @@ def fa_bwd(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int
                               lse or None, dq or None, dk or None, dv or None,
                               workspace or None, workspace_bytes, B, H, Nq, Nk, d,
                               float(scale), int(causal), int(dtype), stream or None)
+
+
+def fa_bwd_ex(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int, dv: int,
+              workspace: int, workspace_bytes: int, B: int, H: int, Nq: int, Nk: int, d: int,
+              scale: float, causal: int, dtype: int, kernels: int, stream: int) -> int:
+    """fa_bwd enqueuing only the kernels in the FA_BWD_* mask; returns the status."""
+    return _lib.load().fa_bwd_ex(q or None, k or None, v or None, o or None, dout or None,
+                                 lse or None, dq or None, dk or None, dv or None,
+                                 workspace or None, workspace_bytes, B, H, Nq, Nk, d,
+                                 float(scale), int(causal), int(dtype), int(kernels), stream or None)
 
 
 def _current_stream(device_index: int):

@@ -23,6 +23,11 @@ FA_PATH_AUTO = 0
 FA_PATH_TILED = 1
 FA_PATH_SHORT = 2
 
+FA_BWD_PRE = 1
+FA_BWD_DKDV = 2
+FA_BWD_DQ = 4
+FA_BWD_ALL = 7
+
 FA_DTYPE_FP16 = 0
 FA_DTYPE_BF16 = 1
 
@@ -62,6 +67,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                            ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
     lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                              ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    lib.fa_bwd_ex.restype = ctypes.c_int
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_launch_error.argtypes = []

@@ -71,6 +71,14 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            const float* lse, void* dq, void* dk, void* dv, void* workspace,
            int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
            float scale, int causal, int dtype, void* stream) {
+  return fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, Nq, Nk, d,
+                   scale, causal, dtype, FA_BWD_ALL, stream);
+}
+
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, void* dq, void* dk, void* dv, void* workspace,
+              int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+              float scale, int causal, int dtype, int kernels, void* stream) {
   // ---- every check happens before the first HIP call
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr ||
       lse == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
@@ -122,6 +130,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
       if (&w2 != &w && fa::overlaps(w.p, w.n, w2.p, w2.n)) return FA_ERR_ALIAS;
   }
 
+  if (kernels < 1 || kernels > FA_BWD_ALL) return FA_ERR_PATH;
+
   fa::BwdParams p;
   p.q = q;
   p.k = k;
@@ -143,21 +153,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   p.scale = scale;
   hipStream_t st = (hipStream_t)stream;
 
-  p.nblk = 0;
-  p.xcd_q = p.xcd_r = 0;
-  hipError_t e = launch(ker.pre, pre_grid, 256, p, st);
-  if (e != hipSuccess) return fa::launch_status(e);
-
-  p.nblk = (int)nkb;
-  p.xcd_q = fa::xcd_split(dkdv_grid).q;
-  p.xcd_r = fa::xcd_split(dkdv_grid).r;
-  e = launch(ker.dkdv, dkdv_grid, ker.dkdv_threads, p, st);
-  if (e != hipSuccess) return fa::launch_status(e);
-
-  p.nblk = (int)nqb;
-  p.xcd_q = fa::xcd_split(dq_grid).q;
-  p.xcd_r = fa::xcd_split(dq_grid).r;
-  e = launch(ker.dq, dq_grid, ker.dq_threads, p, st);
+  hipError_t e = hipSuccess;
+  if (kernels & FA_BWD_PRE) {
+    p.nblk = 0;
+    p.xcd_q = p.xcd_r = 0;
+    e = launch(ker.pre, pre_grid, 256, p, st);
+    if (e != hipSuccess) return fa::launch_status(e);
+  }
+  if (kernels & FA_BWD_DKDV) {
+    p.nblk = (int)nkb;
+    p.xcd_q = fa::xcd_split(dkdv_grid).q;
+    p.xcd_r = fa::xcd_split(dkdv_grid).r;
+    e = launch(ker.dkdv, dkdv_grid, ker.dkdv_threads, p, st);
+    if (e != hipSuccess) return fa::launch_status(e);
+  }
+  if (kernels & FA_BWD_DQ) {
+    p.nblk = (int)nqb;
+    p.xcd_q = fa::xcd_split(dq_grid).q;
+    p.xcd_r = fa::xcd_split(dq_grid).r;
+    e = launch(ker.dq, dq_grid, ker.dq_threads, p, st);
+  }
   return fa::launch_status(e);
 }
 

@@ -53,7 +53,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_ALIGN: return "tensors must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_ALIAS: return "an output overlaps an input, another output or the workspace";
     case FA_ERR_LAUNCH: return "kernel launch failed";
-    case FA_ERR_PATH: return "unknown path, or the short path with too many keys for it";
+    case FA_ERR_PATH: return "unknown path or kernel selection, or the short path with too many keys for it";
     case FA_ERR_WORKSPACE: return "workspace is null, misaligned or smaller than fa_bwd_workspace_bytes";
     default: return "unknown status";
   }

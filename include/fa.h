@@ -54,7 +54,7 @@ enum fa_status {
                       /* workspace                                              */
   FA_ERR_LAUNCH = 9,  /* the kernel launch itself failed (hipGetLastError)      */
   FA_ERR_PATH = 10,   /* fa_fwd_ex: unknown path, or FA_PATH_SHORT with Nk too  */
-                      /* large for it                                           */
+                      /* large for it; fa_bwd_ex: kernel mask not in 1..7       */
   FA_ERR_WORKSPACE = 11 /* fa_bwd: workspace NULL, not 16-byte aligned, or      */
                         /* smaller than fa_bwd_workspace_bytes                  */
 };
@@ -181,6 +181,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            const float* lse, void* dq, void* dk, void* dv, void* workspace,
            int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
            float scale, int causal, int dtype, void* stream);
+
+/* Kernel selection for fa_bwd_ex, a bit mask. fa_bwd runs all three in this
+ * order on one stream. FA_BWD_PRE fills the workspace (per-row D and the
+ * scaled LSE); FA_BWD_DKDV and FA_BWD_DQ read it and are independent of each
+ * other, so a caller may enqueue PRE, then DKDV and DQ on two streams that
+ * both wait for PRE. */
+enum fa_bwd_kernels { FA_BWD_PRE = 1, FA_BWD_DKDV = 2, FA_BWD_DQ = 4, FA_BWD_ALL = 7 };
+
+/*
+ * fa_bwd_ex - fa_bwd enqueuing only the kernels selected in `kernels`
+ * (fa_bwd_kernels bits). Arguments, checks and results are those of fa_bwd;
+ * a mask outside 1..FA_BWD_ALL returns FA_ERR_PATH after the other checks.
+ * DKDV and DQ read the workspace as the last PRE with the same o, dout, lse
+ * and sizes left it: the caller orders them after that PRE.
+ * fa_bwd(...) is fa_bwd_ex(..., FA_BWD_ALL, stream).
+ */
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, void* dq, void* dk, void* dv, void* workspace,
+              int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+              float scale, int causal, int dtype, int kernels, void* stream);
 
 /* A static, human-readable description of a status code (never NULL). */
 const char* fa_status_str(int status);

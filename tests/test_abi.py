@@ -39,7 +39,8 @@ def test_header_enums_match_binding():
     for name in ["FA_OK", "FA_ERR_NULLPTR", "FA_ERR_SHAPE", "FA_ERR_HEADDIM", "FA_ERR_DTYPE",
                  "FA_ERR_SCALE", "FA_ERR_CAUSAL", "FA_ERR_ALIGN", "FA_ERR_ALIAS", "FA_ERR_LAUNCH",
                  "FA_ERR_PATH", "FA_DTYPE_FP16", "FA_DTYPE_BF16", "FA_PATH_AUTO", "FA_PATH_TILED",
-                 "FA_PATH_SHORT", "FA_ERR_WORKSPACE"]:
+                 "FA_PATH_SHORT", "FA_ERR_WORKSPACE", "FA_BWD_PRE", "FA_BWD_DKDV", "FA_BWD_DQ",
+                 "FA_BWD_ALL"]:
         m = re.search(rf"\b{name}\s*=\s*(\d+)", src)
         assert m, name
         assert int(m.group(1)) == getattr(_lib, name), name
@@ -218,3 +219,15 @@ def test_bwd_exact_workspace_is_enough_for_the_checks():
     # then fails a later check (an alias), so nothing is launched
     need = fa.fa_bwd_workspace_bytes(2, 3, 100)
     assert bcall(ws_bytes=need, dv=K) == _lib.FA_ERR_ALIAS
+
+
+@pytest.mark.parametrize("mask", [0, -1, 8, 15])
+def test_bwd_kernel_mask_rejected_before_launch(mask):
+    a = dict(BGOOD)
+    assert fa.fa_bwd_ex(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"],
+                        a["dv"], a["ws"], a["ws_bytes"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                        a["scale"], a["causal"], a["dtype"], mask, None) == _lib.FA_ERR_PATH
+    # the other checks come first
+    assert fa.fa_bwd_ex(0, a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"],
+                        a["dv"], a["ws"], a["ws_bytes"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                        a["scale"], a["causal"], a["dtype"], mask, None) == _lib.FA_ERR_NULLPTR
