@@ -64,15 +64,36 @@ def measured_traffic(key: str, sources=None):
     return ent.get("hbm_bytes_per_launch")
 
 
-def time_gpu(w, steps: int, warmup: int, settle_ms: float = 300.0):
+def layout_inputs(w, layout: str, dev):
+    """q, k, v of w on the device as [B, H, N, d] tensors in a memory layout:
+    "bhnd" contiguous, "bnhd" sequence-major views, "qkv" views of one fused
+    [B, N, 3, H, d] buffer (Nq == Nk); plus an output of the matching layout."""
+    import torch
+
+    from workloads import make_inputs
+
+    q, k, v = make_inputs(w)
+    if layout == "bhnd":
+        q, k, v = (t.to(dev) for t in (q, k, v))
+        return q, k, v, torch.empty_like(q)
+    if layout == "bnhd":
+        q, k, v = (t.transpose(1, 2).contiguous().to(dev).transpose(1, 2) for t in (q, k, v))
+    elif layout == "qkv":
+        qkv = torch.stack([t.transpose(1, 2) for t in (q, k, v)], dim=2).contiguous().to(dev)
+        q, k, v = (qkv[:, :, i].transpose(1, 2) for i in range(3))
+    else:
+        raise ValueError(layout)
+    o = torch.empty((w.B, w.Nq, w.H, w.d), dtype=q.dtype, device=dev).transpose(1, 2)
+    return q, k, v, o
+
+
+def time_gpu(w, steps: int, warmup: int, settle_ms: float = 300.0, layout: str = "bhnd"):
     import torch
 
     import exact_attention_23_amd as fa
-    from workloads import make_inputs
 
     dev = torch.device("cuda:0")
-    q, k, v = (t.to(dev) for t in make_inputs(w))
-    o = torch.empty_like(q)
+    q, k, v, o = layout_inputs(w, layout, dev)
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
     for _ in range(warmup):
         fa.attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
@@ -391,6 +412,10 @@ def main(argv=None):
                     help="fwd (default): the forward line, with the backward of the same "
                          "workload attached; bwd: a line for the backward pass alone")
     ap.add_argument("--no-bwd", action="store_true", help="leave the backward out of the fwd line")
+    ap.add_argument("--layout", choices=("bhnd", "bnhd", "qkv"), default="bhnd",
+                    help="memory layout of q, k, v, o for the forward: contiguous [B,H,N,d] "
+                         "(default), sequence-major [B,N,H,d], or views of a fused [B,N,3,H,d] "
+                         "buffer (the latter two through fa_fwd_strided)")
     args = ap.parse_args(argv)
     if args.write_traffic:
         fd, wd, cfd, cwd, mib = args.write_traffic
@@ -429,7 +454,7 @@ def main(argv=None):
             line["cpu_baseline"] = cpu_baseline_bwd(w)
         print(json.dumps(line), flush=True)
         return 0
-    ms = time_gpu(w, args.steps, args.warmup, args.settle_ms)
+    ms = time_gpu(w, args.steps, args.warmup, args.settle_ms, args.layout)
     tflops = w.flops() / (ms * 1e-3) / 1e12
     n400_us = n400_eager_us = None
     if not args.no_n400 and args.workload != "yolo20":
@@ -452,6 +477,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                    "causal": w.causal, "input_dtype": w.dtype, "accumulate": "fp32",
+                   "layout": args.layout,
                    "parallelism": "single GPU; grid over (batch, head, query block)"},
         "us_per_call": round(ms * 1e3, 3),
         # N=400 (20x20 map): device time per call from a replayed HIP graph of

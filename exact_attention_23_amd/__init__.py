@@ -7,6 +7,7 @@ missing library or an unsupported argument raises.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 from typing import Optional, Tuple
 
@@ -14,7 +15,7 @@ from . import _lib
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_FP16, FA_OK, FA_PATH_AUTO,  # noqa: F401
                    FA_PATH_SHORT, FA_PATH_TILED)
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_ex", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_bytes", "attention",
+__all__ = ["FaError", "fa_fwd", "fa_fwd_ex", "fa_fwd_strided", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_bytes", "attention",
            "attention_backward", "flash_attention", "version"]
 
 _PATHS = {"auto": FA_PATH_AUTO, "tiled": FA_PATH_TILED, "short": FA_PATH_SHORT}
@@ -47,6 +48,17 @@ def fa_fwd_ex(q: int, k: int, v: int, o: int, lse: Optional[int], B: int, H: int
     """fa_fwd with an explicit kernel choice (FA_PATH_*); returns the status."""
     return _lib.load().fa_fwd_ex(q, k, v, o, lse or None, B, H, Nq, Nk, d, float(scale),
                                  int(causal), int(dtype), int(path), stream or None)
+
+
+def fa_fwd_strided(q: int, k: int, v: int, o: int, lse: Optional[int], B: int, H: int, Nq: int,
+                   Nk: int, d: int, strides, scale: float, causal: int, dtype: int,
+                   stream: int) -> int:
+    """fa_fwd on tensors in any layout with contiguous d: `strides` is 12 element
+    strides (q, k, v, o; each batch, head, row); returns the status."""
+    arr = None if strides is None else (ctypes.c_int64 * 12)(*strides)
+    return _lib.load().fa_fwd_strided(q, k, v, o, lse or None, B, H, Nq, Nk, d,
+                                      None if arr is None else ctypes.cast(arr, ctypes.c_void_p),
+                                      float(scale), int(causal), int(dtype), stream or None)
 
 
 def fa_bwd_workspace_bytes(B: int, H: int, Nq: int) -> int:
@@ -98,23 +110,36 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}: fp16 or bf16 expected")
 
 
+def _layout_strides(t, name):
+    """(batch, head, row) element strides of a [B, H, N, d] GPU tensor whose
+    last dimension is contiguous."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError(f"{name} must be a [B, H, N, d] tensor with contiguous d")
+    return [t.stride(0), t.stride(1), t.stride(2)]
+
+
 def attention(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
               out=None, lse=None, return_lse: bool = True, path: str = "auto"):
     """O = softmax(scale * Q K^T [causal mask]) V on the GPU, plus LSE.
 
-    q: [B, H, Nq, d], k and v: [B, H, Nk, d], contiguous fp16/bf16 CUDA (HIP)
-    tensors on one device. scale=None means 1/sqrt(d). Returns (out, lse) with
-    lse [B, H, Nq] float32, or (out, None) when return_lse is False. The work
+    q: [B, H, Nq, d], k and v: [B, H, Nk, d], fp16/bf16 CUDA (HIP) tensors
+    on one device. Contiguous tensors go through fa_fwd_ex; any other layout
+    with a contiguous last dimension (e.g. [B, N, H, d] transposed to
+    [B, H, N, d], or views of a fused [B, N, 3, H, d] projection) through
+    fa_fwd_strided, read in place. scale=None means 1/sqrt(d). Returns (out,
+    lse) with lse [B, H, Nq] float32, or (out, None) when return_lse is
+    False; out gets q's layout when q is dense, else is contiguous. The work
     is enqueued on the current stream of q's device. path selects the kernel
-    ("auto", "tiled" or "short"; see fa_path in include/fa.h).
+    ("auto", "tiled" or "short"; see fa_path in include/fa.h) and is only
+    available for contiguous tensors.
     """
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
-        if t.dim() != 4 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be a [B, H, N, d] tensor")
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on one device")
     if not (q.dtype == k.dtype == v.dtype):
@@ -129,27 +154,36 @@ def attention(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
-        out = torch.empty_like(q)
-    elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device
-          or not out.is_contiguous()):
-        raise ValueError("out must be a contiguous tensor like q")
+        out = torch.empty_like(q)  # q's strides when q is dense, else contiguous
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device:
+        raise ValueError("out must be a tensor like q")
     if lse is None and return_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     elif lse is not None and (tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32
                               or lse.device != q.device or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
     lib = _lib.load()
-    call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-            lse.data_ptr() if lse is not None else None,
-            B, H, Nq, Nk, d, float(scale), 1 if causal else 0, code, _PATHS[path])
+    contiguous = q.is_contiguous() and k.is_contiguous() and v.is_contiguous() and out.is_contiguous()
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            lse.data_ptr() if lse is not None else None, B, H, Nq, Nk, d)
+    tail = (float(scale), 1 if causal else 0, code)
+    if contiguous:
+        fn, call = lib.fa_fwd_ex, ptrs + tail + (_PATHS[path],)
+    else:
+        if path != "auto":
+            raise ValueError("path applies to contiguous tensors only")
+        strides = (_layout_strides(q, "q") + _layout_strides(k, "k") + _layout_strides(v, "v")
+                   + _layout_strides(out, "out"))
+        arr = (ctypes.c_int64 * 12)(*strides)
+        fn, call = lib.fa_fwd_strided, ptrs + (ctypes.cast(arr, ctypes.c_void_p),) + tail
     # The launch goes to the current device; switch only when q lives elsewhere
     # (the device guard costs several microseconds per call).
     idx = q.device.index
     if idx == torch.cuda.current_device():
-        st = lib.fa_fwd_ex(*call, _current_stream(idx))
+        st = fn(*call, _current_stream(idx))
     else:
         with torch.cuda.device(q.device):
-            st = lib.fa_fwd_ex(*call, _current_stream(idx))
+            st = fn(*call, _current_stream(idx))
     _check(st)
     return out, lse
 

@@ -18,6 +18,7 @@ FA_ERR_ALIAS = 8
 FA_ERR_LAUNCH = 9
 FA_ERR_PATH = 10
 FA_ERR_WORKSPACE = 11
+FA_ERR_STRIDE = 12
 
 FA_PATH_AUTO = 0
 FA_PATH_TILED = 1
@@ -62,6 +63,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                               ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     lib.fa_fwd_ex.restype = ctypes.c_int
+    lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp,
+                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+    lib.fa_fwd_strided.restype = ctypes.c_int
     lib.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
     lib.fa_bwd_workspace_bytes.restype = i64
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,

@@ -86,9 +86,57 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   return fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, FA_PATH_AUTO, stream);
 }
 
-int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
-              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
-              float scale, int causal, int dtype, int path, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// One tensor's layout as the caller gives it (element strides; d contiguous).
+struct Layout {
+  int64_t b, h, n;
+};
+
+// Bytes from a tensor's first element to one past its last.
+int64_t span_bytes(const Layout& s, int64_t B, int64_t H, int64_t N, int64_t d) {
+  return ((B - 1) * s.b + (H - 1) * s.h + (N - 1) * s.n + d) * 2;
+}
+
+// A layout the kernels can address: 16-byte aligned rows and heads, rows at
+// least d apart, per-head spans within 32-bit byte offsets (with room for a
+// tile read past the last row).
+bool layout_ok(const Layout& s, int64_t N, int64_t d) {
+  if (s.b < 0 || s.h < 0 || s.n < d) return false;
+  if ((s.b | s.h | s.n) & 7) return false;
+  const int64_t lim = (int64_t)1 << 30;
+  if (s.n >= lim || (N - 1) * s.n + d >= lim / 2 || (N + 256) * s.n * 2 >= 2 * lim) return false;
+  return true;
+}
+
+// No two elements of an output share an address: sorted by stride, every
+// dimension of extent > 1 must step past everything the inner ones cover.
+bool injective(const Layout& s, int64_t B, int64_t H, int64_t N, int64_t d) {
+  int64_t dims[3][2] = {{s.b, B}, {s.h, H}, {s.n, N}};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (dims[j][0] < dims[i][0]) {
+        for (int c = 0; c < 2; ++c) {
+          const int64_t t = dims[i][c];
+          dims[i][c] = dims[j][c];
+          dims[j][c] = t;
+        }
+      }
+  int64_t extent = d;
+  for (int i = 0; i < 3; ++i) {
+    if (dims[i][1] <= 1) continue;
+    if (dims[i][0] < extent) return false;
+    extent = dims[i][0] * (dims[i][1] - 1) + extent;
+  }
+  return true;
+}
+
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+             float scale, int causal, int dtype, int path, bool strided, const int64_t* strides,
+             void* stream) {
   // ---- every check happens before the first HIP call
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_NULLPTR;
   if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
@@ -105,22 +153,39 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
   if (((uintptr_t)lse) & 3u) return FA_ERR_ALIGN;
 
+  // Layouts: the given element strides, or contiguous [B, H, N, d].
+  Layout sq{H * Nq * d, Nq * d, d}, sk{H * Nk * d, Nk * d, d}, sv = sk, so = sq;
+  if (strided) {
+    if (strides == nullptr) return FA_ERR_STRIDE;
+    sq = {strides[0], strides[1], strides[2]};
+    sk = {strides[3], strides[4], strides[5]};
+    sv = {strides[6], strides[7], strides[8]};
+    so = {strides[9], strides[10], strides[11]};
+    if (!layout_ok(sq, Nq, d) || !layout_ok(sk, Nk, d) || !layout_ok(sv, Nk, d) ||
+        !layout_ok(so, Nq, d) || !injective(so, B, H, Nq, d))
+      return FA_ERR_STRIDE;
+  }
+
   const Variant var = dtype == FA_DTYPE_FP16 ? pick<_Float16>(d, causal != 0)
                                              : pick<__bf16>(d, causal != 0);
   const int64_t num_qb = (Nq + var.bm - 1) / var.bm;
   const int64_t total = B * H * num_qb;
   if (total >= lim) return FA_ERR_SHAPE;
 
-  const size_t es = 2;
-  const size_t qo_bytes = (size_t)(B * H) * (size_t)(Nq * d) * es;
-  const size_t kv_bytes = (size_t)(B * H) * (size_t)(Nk * d) * es;
+  // o and lse are written: neither may overlap an input or the other (byte
+  // spans from first to last element, so interleaved layouts count as
+  // overlapping).
+  const size_t q_bytes = (size_t)span_bytes(sq, B, H, Nq, d);
+  const size_t k_bytes = (size_t)span_bytes(sk, B, H, Nk, d);
+  const size_t v_bytes = (size_t)span_bytes(sv, B, H, Nk, d);
+  const size_t o_bytes = (size_t)span_bytes(so, B, H, Nq, d);
   const size_t lse_bytes = (size_t)(B * H) * (size_t)Nq * 4;
-  if (fa::overlaps(o, qo_bytes, q, qo_bytes) || fa::overlaps(o, qo_bytes, k, kv_bytes) ||
-      fa::overlaps(o, qo_bytes, v, kv_bytes))
+  if (fa::overlaps(o, o_bytes, q, q_bytes) || fa::overlaps(o, o_bytes, k, k_bytes) ||
+      fa::overlaps(o, o_bytes, v, v_bytes))
     return FA_ERR_ALIAS;
   if (lse != nullptr &&
-      (fa::overlaps(lse, lse_bytes, q, qo_bytes) || fa::overlaps(lse, lse_bytes, k, kv_bytes) ||
-       fa::overlaps(lse, lse_bytes, v, kv_bytes) || fa::overlaps(lse, lse_bytes, o, qo_bytes)))
+      (fa::overlaps(lse, lse_bytes, q, q_bytes) || fa::overlaps(lse, lse_bytes, k, k_bytes) ||
+       fa::overlaps(lse, lse_bytes, v, v_bytes) || fa::overlaps(lse, lse_bytes, o, o_bytes)))
     return FA_ERR_ALIAS;
   if (path != FA_PATH_AUTO && path != FA_PATH_TILED && path != FA_PATH_SHORT) return FA_ERR_PATH;
   const int64_t key_tiles = (Nk + 63) / 64;
@@ -150,6 +215,10 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
   p.xcd_r = (int)(total % 8);
   p.group = 1;
   p.nkt = (int)key_tiles;
+  p.sq = {sq.b, sq.h, (int)sq.n};
+  p.sk = {sk.b, sk.h, (int)sk.n};
+  p.sv = {sv.b, sv.h, (int)sv.n};
+  p.so = {so.b, so.h, (int)so.n};
   if (scale == 0.0f) {  // every logit is 0: zero Q, any positive factor works
     p.c = 1.0f;
     p.q_and = 0u;
@@ -174,6 +243,24 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                         (hipStream_t)stream);
   }
   return fa::launch_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+              float scale, int causal, int dtype, int path, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, path, false, nullptr,
+                  stream);
+}
+
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                   const int64_t* strides, float scale, int causal, int dtype, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, FA_PATH_AUTO, true,
+                  strides, stream);
 }
 
 }  // extern "C"

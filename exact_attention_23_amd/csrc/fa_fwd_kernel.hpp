@@ -61,6 +61,13 @@
 
 namespace fa {
 
+// Element strides of one [B, H, N, d] tensor: batch, head and row (the d
+// elements of a row are contiguous). Contiguous tensors have (H*N*d, N*d, d).
+struct Strides {
+  int64_t b, h;
+  int n;
+};
+
 struct Params {
   const void* q;
   const void* k;
@@ -77,7 +84,19 @@ struct Params {
   uint32_t q_and; // applied to each 32-bit word of Q: ~0 normally, 0 when scale == 0
   uint32_t q_xor; // 0x80008000 flips both halves' sign when scale < 0
   int nkt;        // short-range kernel: 64-key tiles (= waves) per workgroup
+  Strides sq, sk, sv, so;  // layouts of q, k, v and o
 };
+
+// First element of head (b, h) of a tensor, and the bytes a buffer resource
+// over its n rows must cover (rows past n then read as zero).
+template <typename T>
+__device__ __forceinline__ T* head_base(const void* base, const Strides& s, int b, int h) {
+  return (T*)base + (int64_t)b * s.b + (int64_t)h * s.h;
+}
+template <int D>
+__device__ __forceinline__ int head_bytes(int n, const Strides& s) {
+  return ((n - 1) * s.n + D) * 2;
+}
 
 // Largest tile row sum, relative to the reference maximum, that is accepted
 // without raising the maximum (see the file comment). Every P of the tile is
@@ -150,14 +169,14 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   const int r32 = lane & 31;   // this lane's query within a 32-row block
 
   const int Nq = p.Nq, Nk = p.Nk;
-  const size_t q_head = (size_t)head * Nq * D;
-  const size_t kv_head = (size_t)head * Nk * D;
+  const int hb = head / p.H, hh = head - hb * p.H;
+  const int qrs = 2 * p.sq.n, krs = 2 * p.sk.n, vrs = 2 * p.sv.n;  // row strides in bytes
   const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const T*)p.q + q_head), (short)0, Nq * D * 2, kBufferFlags);
+      (void*)head_base<const T>(p.q, p.sq, hb, hh), (short)0, head_bytes<D>(Nq, p.sq), kBufferFlags);
   const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const T*)p.k + kv_head), (short)0, Nk * D * 2, kBufferFlags);
+      (void*)head_base<const T>(p.k, p.sk, hb, hh), (short)0, head_bytes<D>(Nk, p.sk), kBufferFlags);
   const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const T*)p.v + kv_head), (short)0, Nk * D * 2, kBufferFlags);
+      (void*)head_base<const T>(p.v, p.sv, hb, hh), (short)0, head_bytes<D>(Nk, p.sv), kBufferFlags);
 
   const int wave_q0 = qb * BM + wave * WR;
 
@@ -169,7 +188,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
-          q_rsrc, row * (2 * D) + 2 * (16 * s + 8 * half), 0, 0);
+          q_rsrc, row * qrs + 2 * (16 * s + 8 * half), 0, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = (w[e] & p.q_and) ^ p.q_xor;
       qf[rb][s] = __builtin_bit_cast(vec, w);
@@ -222,8 +241,8 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
     const int r = sl / CPR;
     const int ch = (lds_off<2 * D>(r, sl % CPR) - r * (2 * D)) >> 4;  // logical chunk
     const int kkey = (r & ~31) | lds_row_to_key(r & 31);
-    k_goff[i] = kkey * (2 * D) + 16 * ch;
-    v_goff[i] = r * (2 * D) + 16 * ch;
+    k_goff[i] = kkey * krs + 16 * ch;
+    v_goff[i] = r * vrs + 16 * ch;
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
   // Offsets of tiles past the end are pushed beyond every buffer's range:
@@ -231,14 +250,15 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   constexpr uint32_t kOutOfRange = 0x40000000u;
   auto issue = [&](int t) {
     const int st = t % S;
-    const uint32_t gbase = t < ntiles ? (uint32_t)(t * TILE_BYTES) : kOutOfRange;
+    const uint32_t kbase = t < ntiles ? (uint32_t)(t * BN * krs) : kOutOfRange;
+    const uint32_t vbase = t < ntiles ? (uint32_t)(t * BN * vrs) : kOutOfRange;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const uint32_t blk = (uint32_t)((wave * CPT + i) * 1024);
       dma_to_lds(k_rsrc, __builtin_amdgcn_readfirstlane(lds_base + (2 * st) * TILE_BYTES + blk),
-                 k_goff[i] + gbase);
+                 k_goff[i] + kbase);
       dma_to_lds(v_rsrc, __builtin_amdgcn_readfirstlane(lds_base + (2 * st + 1) * TILE_BYTES + blk),
-                 v_goff[i] + gbase);
+                 v_goff[i] + vbase);
     }
   };
 
@@ -603,7 +623,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
     const float l_tot = M::kMfmaRowSum ? l_run[rb] : sum_with_partner(l_run[rb]);
     const float inv = 1.0f / l_tot;
     if (q_row < Nq) {
-      T* Oh = (T*)p.o + q_head + (size_t)q_row * D;
+      T* Oh = head_base<T>(p.o, p.so, hb, hh) + (int64_t)q_row * p.so.n;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll

@@ -60,14 +60,14 @@ __global__ __launch_bounds__(1024) void fa_fwd_short_kernel(Params p) {
   const int r32 = lane & 31;
   const int Nq = p.Nq, Nk = p.Nk, nw = p.nkt;
 
-  const size_t q_head = (size_t)head * Nq * D;
-  const size_t kv_head = (size_t)head * Nk * D;
+  const int hb = head / p.H, hh = head - hb * p.H;
+  const int qrs = 2 * p.sq.n, krs = 2 * p.sk.n, vrs = 2 * p.sv.n;  // row strides in bytes
   const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const T*)p.q + q_head), (short)0, Nq * D * 2, kBufferFlags);
+      (void*)head_base<const T>(p.q, p.sq, hb, hh), (short)0, head_bytes<D>(Nq, p.sq), kBufferFlags);
   const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const T*)p.k + kv_head), (short)0, Nk * D * 2, kBufferFlags);
+      (void*)head_base<const T>(p.k, p.sk, hb, hh), (short)0, head_bytes<D>(Nk, p.sk), kBufferFlags);
   const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const T*)p.v + kv_head), (short)0, Nk * D * 2, kBufferFlags);
+      (void*)head_base<const T>(p.v, p.sv, hb, hh), (short)0, head_bytes<D>(Nk, p.sv), kBufferFlags);
 
   const int q0 = qb * 32;
   const int q_row = q0 + r32;
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(1024) void fa_fwd_short_kernel(Params p) {
       const int r = sl / CPR;
       const int ch = (lds_off<2 * D>(r, sl % CPR) - r * (2 * D)) >> 4;  // logical chunk
       dma_to_lds(v_rsrc, __builtin_amdgcn_readfirstlane(lds_v + i * 1024),
-                 (uint32_t)((kb + r) * (2 * D) + 16 * ch));
+                 (uint32_t)((kb + r) * vrs + 16 * ch));
     }
   }
 
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(1024) void fa_fwd_short_kernel(Params p) {
   vec qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, q_row * (2 * D) + 2 * (16 * s + 8 * half),
+    u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, q_row * qrs + 2 * (16 * s + 8 * half),
                                                     0, 0);
 #pragma unroll
     for (int e = 0; e < 4; ++e) w[e] = (w[e] & p.q_and) ^ p.q_xor;
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(1024) void fa_fwd_short_kernel(Params p) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const vec a = __builtin_bit_cast(
-          vec, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, krow * (2 * D) + 2 * (16 * s + 8 * half), 0, 0));
+          vec, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, krow * krs + 2 * (16 * s + 8 * half), 0, 0));
       sacc[t] = M::run(a, qf[s], s == 0 ? f32x16{} : sacc[t]);
     }
   }
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(1024) void fa_fwd_short_kernel(Params p) {
   __syncthreads();
 
   // ---- sum the partials (two adjacent d per thread), normalise, store
-  T* Oh = (T*)p.o + q_head;
+  T* Oh = head_base<T>(p.o, p.so, hb, hh);
   for (int e = tid; e < 16 * D; e += 64 * nw) {
     const int r = (2 * e) / D, d = (2 * e) % D;
     if (q0 + r >= Nq) continue;
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(1024) void fa_fwd_short_kernel(Params p) {
       a1 += pw[1];
     }
     const float inv = 1.0f / s_L[r];
-    *(pair*)(Oh + (size_t)(q0 + r) * D + d) = M::cvt(a0 * inv, a1 * inv);
+    *(pair*)(Oh + (int64_t)(q0 + r) * p.so.n + d) = M::cvt(a0 * inv, a1 * inv);
   }
   if (p.lse != nullptr && tid < 32 && q0 + tid < Nq)
     p.lse[(size_t)head * Nq + q0 + tid] = 0.69314718055994531f * (s_M[tid] + log2f(s_L[tid]));

@@ -54,6 +54,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_ALIAS: return "an output overlaps an input, another output or the workspace";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_PATH: return "unknown path or kernel selection, or the short path with too many keys for it";
+    case FA_ERR_STRIDE: return "strides missing, misaligned, overlapping or too large for one head";
     case FA_ERR_WORKSPACE: return "workspace is null, misaligned or smaller than fa_bwd_workspace_bytes";
     default: return "unknown status";
   }

@@ -55,8 +55,10 @@ enum fa_status {
   FA_ERR_LAUNCH = 9,  /* the kernel launch itself failed (hipGetLastError)      */
   FA_ERR_PATH = 10,   /* fa_fwd_ex: unknown path, or FA_PATH_SHORT with Nk too  */
                       /* large for it; fa_bwd_ex: kernel mask not in 1..7       */
-  FA_ERR_WORKSPACE = 11 /* fa_bwd: workspace NULL, not 16-byte aligned, or      */
-                        /* smaller than fa_bwd_workspace_bytes                  */
+  FA_ERR_WORKSPACE = 11, /* fa_bwd: workspace NULL, not 16-byte aligned, or     */
+                         /* smaller than fa_bwd_workspace_bytes                 */
+  FA_ERR_STRIDE = 12  /* fa_fwd_strided: strides NULL, or a layout the kernels  */
+                      /* cannot address (see fa_fwd_strided)                    */
 };
 
 /* Element types of q, k, v and o (all four share one type). Accumulation is
@@ -121,6 +123,33 @@ enum fa_path { FA_PATH_AUTO = 0, FA_PATH_TILED = 1, FA_PATH_SHORT = 2 };
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
               float scale, int causal, int dtype, int path, void* stream);
+
+/*
+ * fa_fwd_strided - fa_fwd on tensors in any [B, H, N, d] layout whose d
+ * elements are contiguous: for example [B, N, H, d] (sequence-major, the
+ * layout of a projection's output reshaped into heads) or q, k, v as views
+ * of one fused [B, N, 3, H, d] projection output. The layout and fusion
+ * variants of the kwkr.cn YOLO11 FlashAttention-2 article, section 2.2 (the
+ * transposes around the attention call) and of "FlashAttention 深度解读",
+ * section 实现 2 (fused operator), are then read in place, with no copies.
+ *
+ *   strides  host array of 12 int64 element strides, in the order
+ *            q: batch, head, row;  k: batch, head, row;
+ *            v: batch, head, row;  o: batch, head, row.
+ *            Element (b, h, n, c) of q is at q + b*s0 + h*s1 + n*s2 + c.
+ *            Every stride is a multiple of 8 elements (16 bytes) and >= 0;
+ *            row strides are >= d; one head's rows span fewer than 2^29
+ *            elements. o's layout must map distinct elements to distinct
+ *            addresses. Violations return FA_ERR_STRIDE.
+ *   lse      stays contiguous [B, H, Nq] fp32 (or NULL).
+ * Everything else (arguments, results, error behaviour) is as in fa_fwd; the
+ * kernel choice is FA_PATH_AUTO. Overlap checks use each tensor's byte span
+ * from its first to its last element, so o interleaved with an input counts
+ * as overlapping (FA_ERR_ALIAS).
+ */
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                   const int64_t* strides, float scale, int causal, int dtype, void* stream);
 
 /*
  * Backward pass. For an upstream gradient dO of the forward's output O, the
