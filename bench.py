@@ -32,11 +32,15 @@ METRIC = "attention fwd TFLOP/s and % MFMA peak; µs/call at N=400 and N=6400"
 # MI355X dense fp16/bf16 matrix peak: 256 CUs x 4096 FLOP/clk x 2.4 GHz.
 PEAK_MFMA_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
+# MI355X dense fp8 matrix peak (twice the fp16 rate)
+PEAK_MFMA_FP8_TFLOPS = 5033.2
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_23_amd", "csrc", f)
                   for f in ("fa_device.hpp", "fa_fwd_kernel.hpp", "fa_fwd_short.hpp", "fa_api.hip")]
 BWD_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_23_amd", "csrc", f)
                       for f in ("fa_device.hpp", "fa_bwd_kernel.hpp", "fa_bwd.hip")]
+FP8_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_23_amd", "csrc", f)
+                      for f in ("fa_device.hpp", "fa_fwd_kernel.hpp", "fa_fwd_fp8.hpp", "fa_fp8.hip")]
 # backward kernels as rocprofv3 names them, and the FA_BWD_* bit of each
 BWD_KERNELS = (("pre", "fa_bwd_pre_kernel", 1), ("dkdv", "fa_bwd_dkdv_kernel", 2),
                ("dq", "fa_bwd_dq_kernel", 4))
@@ -118,6 +122,42 @@ def time_gpu(w, steps: int, warmup: int, settle_ms: float = 300.0, layout: str =
     if not torch.isfinite(o.float()).all():
         raise RuntimeError("non-finite output in the timed run")
     return ms
+
+
+def time_fp8(w, steps: int, warmup: int, settle_ms: float = 300.0):
+    """ms per FP8 forward call on w's inputs quantised to e4m3 (bf16 output)."""
+    import torch
+
+    import exact_attention_23_amd as fa
+    from workloads import make_inputs_fp8
+
+    dev = torch.device("cuda:0")
+    q8, k8, v8, sq, sk, sv = make_inputs_fp8(w)
+    q8, k8, v8 = (t.to(dev) for t in (q8, k8, v8))
+    o = torch.empty((w.B, w.H, w.Nq, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+
+    def call():
+        fa.attention_fp8(q8, k8, v8, sq, sk, sv, causal=w.causal, scale=w.scale, out=o, lse=lse)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(8):
+            call()
+        torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        call()
+    ev1.record()
+    torch.cuda.synchronize()
+    if not torch.isfinite(o.float()).all():
+        raise RuntimeError("non-finite output in the timed run")
+    return ev0.elapsed_time(ev1) / steps
 
 
 def time_graph(w, calls: int = 100, replays: int = 20):
@@ -412,6 +452,9 @@ def main(argv=None):
                     help="fwd (default): the forward line, with the backward of the same "
                          "workload attached; bwd: a line for the backward pass alone")
     ap.add_argument("--no-bwd", action="store_true", help="leave the backward out of the fwd line")
+    ap.add_argument("--fp8", action="store_true",
+                    help="forward on the workload's inputs quantised to e4m3 (fa_fwd_fp8), "
+                         "against the fp8 matrix peak")
     ap.add_argument("--layout", choices=("bhnd", "bnhd", "qkv"), default="bhnd",
                     help="memory layout of q, k, v, o for the forward: contiguous [B,H,N,d] "
                          "(default), sequence-major [B,N,H,d], or views of a fused [B,N,3,H,d] "
@@ -452,6 +495,26 @@ def main(argv=None):
         }
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline_bwd(w)
+        print(json.dumps(line), flush=True)
+        return 0
+    if args.fp8:
+        ms = time_fp8(w, args.steps, args.warmup, args.settle_ms)
+        tflops = w.flops() / (ms * 1e-3) / 1e12
+        line = {
+            "metric": "attention fwd TFLOP/s on FP8 (e4m3) inputs and % fp8 MFMA peak",
+            "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+            "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                       "causal": w.causal, "input_dtype": "fp8_e4m3 (per-tensor amax scaling)",
+                       "output_dtype": "bf16", "accumulate": "fp32",
+                       "parallelism": "single GPU; grid over (batch, head, query block)"},
+            "us_per_call": round(ms * 1e3, 3),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_MFMA_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_FP8_TFLOPS, 4),
+                         "traffic": None},
+            "kernel_source_sha": kernel_source_hash(FP8_KERNEL_SOURCES),
+        }
         print(json.dumps(line), flush=True)
         return 0
     ms = time_gpu(w, args.steps, args.warmup, args.settle_ms, args.layout)

@@ -15,7 +15,7 @@ from . import _lib
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_FP16, FA_OK, FA_PATH_AUTO,  # noqa: F401
                    FA_PATH_SHORT, FA_PATH_TILED)
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_ex", "fa_fwd_strided", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_bytes", "attention",
+__all__ = ["FaError", "fa_fwd", "fa_fwd_ex", "fa_fwd_strided", "attention_fp8", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_bytes", "attention",
            "attention_backward", "flash_attention", "version"]
 
 _PATHS = {"auto": FA_PATH_AUTO, "tiled": FA_PATH_TILED, "short": FA_PATH_SHORT}
@@ -184,6 +184,61 @@ def attention(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
     else:
         with torch.cuda.device(q.device):
             st = fn(*call, _current_stream(idx))
+    _check(st)
+    return out, lse
+
+
+def attention_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float, *,
+                  causal: bool = False, scale: Optional[float] = None, out_dtype=None,
+                  out=None, lse=None, return_lse: bool = True):
+    """Attention on FP8 (e4m3) q, k, v with per-tensor dequantisation factors.
+
+    q: [B, H, Nq, d], k and v: [B, H, Nk, d], contiguous torch.float8_e4m3fn
+    GPU tensors, d = 64 or 128; element x of q means q_descale * x (likewise
+    k, v). Returns (out, lse): out [B, H, Nq, d] in out_dtype (torch.bfloat16
+    by default, or torch.float16), lse [B, H, Nq] float32 (None when
+    return_lse is False). scale=None means 1/sqrt(d).
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float8_e4m3fn:
+            raise ValueError(f"{name} must be a float8_e4m3fn GPU tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
+        raise ValueError("k and v must be [B, H, Nk, d] matching q")
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.bfloat16
+    code = {torch.float16: FA_DTYPE_FP16, torch.bfloat16: FA_DTYPE_BF16}.get(out_dtype)
+    if code is None:
+        raise TypeError("out_dtype must be torch.float16 or torch.bfloat16")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
+    elif (tuple(out.shape) != (B, H, Nq, d) or out.dtype != out_dtype or out.device != q.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous [B, H, Nq, d] tensor of out_dtype")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    elif lse is not None and (tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32
+                              or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    lib = _lib.load()
+    call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            lse.data_ptr() if lse is not None else None, B, H, Nq, Nk, d, float(scale),
+            float(q_descale), float(k_descale), float(v_descale), 1 if causal else 0, code)
+    idx = q.device.index
+    if idx == torch.cuda.current_device():
+        st = lib.fa_fwd_fp8(*call, _current_stream(idx))
+    else:
+        with torch.cuda.device(q.device):
+            st = lib.fa_fwd_fp8(*call, _current_stream(idx))
     _check(st)
     return out, lse
 

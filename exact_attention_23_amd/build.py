@@ -18,9 +18,10 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 ARCH = "gfx950"
-SOURCES = [os.path.join(CSRC, f) for f in ("fa_lib.hip", "fa_api.hip", "fa_bwd.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("fa_lib.hip", "fa_api.hip", "fa_bwd.hip", "fa_fp8.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("fa_device.hpp", "fa_host.hpp", "fa_fwd_kernel.hpp",
-                                          "fa_fwd_short.hpp", "fa_bwd_kernel.hpp")] + [
+                                          "fa_fwd_short.hpp", "fa_bwd_kernel.hpp",
+                                          "fa_fwd_fp8.hpp")] + [
     os.path.join(os.path.dirname(PKG_DIR), "include", "fa.h")]
 
 

@@ -152,6 +152,33 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
                    const int64_t* strides, float scale, int causal, int dtype, void* stream);
 
 /*
+ * fa_fwd_fp8 - exact attention forward on FP8 inputs (FlashAttention-3's FP8
+ * variant, ai2ai.xin flash-attention-principle page, FA-3 section).
+ *
+ *   q, k, v    [B, H, N, d] contiguous, one byte per element: OCP e4m3 ("fn":
+ *              no infinities; bytes 0x7f and 0xff are NaN and must not occur)
+ *   q_descale, k_descale, v_descale
+ *              per-tensor dequantisation factors (> 0, finite): element x of q
+ *              stands for q_descale * e4m3(x), and likewise for k and v
+ *   o          [B, H, Nq, d] contiguous output in out_dtype (FA_DTYPE_FP16 or
+ *              FA_DTYPE_BF16)
+ *   lse, B, H, Nq, Nk, scale, causal, stream: as in fa_fwd
+ *   d          64 or 128
+ * Computes the forward of the dequantised tensors: S = scale * q_descale *
+ * k_descale * (Q K^T on the e4m3 values, fp32 accumulation), O = softmax(S) V.
+ * The attention weights are rounded to e4m3 (after scaling so that the
+ * largest weight of a row is 2^8) for the P V product on the FP8 matrix cores;
+ * the row sum and the LSE use the unrounded fp32 weights. Errors: FA_ERR_DTYPE
+ * for out_dtype, FA_ERR_HEADDIM for d = 32, FA_ERR_SCALE for a descale factor
+ * that is not finite and positive or a product with scale that overflows;
+ * otherwise as fa_fwd. Deterministic (no atomics).
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+               float q_descale, float k_descale, float v_descale, int causal, int out_dtype,
+               void* stream);
+
+/*
  * Backward pass. For an upstream gradient dO of the forward's output O, the
  * gradients of the scalar sum(O * dO) with respect to Q, K and V, per (b, h):
  *

@@ -280,3 +280,38 @@ def test_strided_alias_uses_spans():
     fused = [100 * 3 * 3 * 64, 64, 3 * 3 * 64] * 3 + [100 * 3 * 64, 64, 3 * 64]
     assert scall(fused, B=2, H=3, Nq=100, Nk=100, k=Q + 3 * 64 * 2, v=Q + 6 * 64 * 2,
                  o=Q + 64) == _lib.FA_ERR_ALIAS
+
+
+# ---- FP8 forward
+FGOOD = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, Nq=100, Nk=77, d=64, scale=0.125,
+             qd=0.01, kd=0.02, vd=0.03, causal=0, out_dtype=1, stream=None)
+
+
+def fcall(**kw):
+    a = dict(FGOOD)
+    a.update(kw)
+    return _lib.load().fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                                  a["Nk"], a["d"], a["scale"], a["qd"], a["kd"], a["vd"], a["causal"],
+                                  a["out_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), _lib.FA_ERR_NULLPTR),
+    (dict(o=None), _lib.FA_ERR_NULLPTR),
+    (dict(out_dtype=2), _lib.FA_ERR_DTYPE),
+    (dict(d=32), _lib.FA_ERR_HEADDIM),
+    (dict(d=96), _lib.FA_ERR_HEADDIM),
+    (dict(Nq=0), _lib.FA_ERR_SHAPE),
+    (dict(causal=2), _lib.FA_ERR_CAUSAL),
+    (dict(qd=0.0), _lib.FA_ERR_SCALE),
+    (dict(kd=-1.0), _lib.FA_ERR_SCALE),
+    (dict(vd=float("nan")), _lib.FA_ERR_SCALE),
+    (dict(scale=float("inf")), _lib.FA_ERR_SCALE),
+    (dict(scale=1e30, qd=1e30), _lib.FA_ERR_SCALE),
+    (dict(k=K + 8), _lib.FA_ERR_ALIGN),
+    (dict(lse=L + 1), _lib.FA_ERR_ALIGN),
+    (dict(o=Q + 1024), _lib.FA_ERR_ALIAS),
+    (dict(lse=O + 64), _lib.FA_ERR_ALIAS),
+])
+def test_fp8_invalid_arguments_rejected_before_launch(kw, status):
+    assert fcall(**kw) == status

@@ -109,6 +109,34 @@ def make_inputs(w: Workload, seed: Optional[int] = None):
     return q.contiguous(), k.contiguous(), v.contiguous()
 
 
+FP8_MAX = 448.0  # largest finite e4m3 ("fn") value
+
+
+def make_inputs_fp8(w: Workload, seed: Optional[int] = None):
+    """The same float32 draws as make_inputs (q, then k, then v from one
+    generator), quantised per tensor to e4m3 the usual way: descale =
+    max|x| / 448 in float32, stored = e4m3(x / descale) (round to nearest even,
+    torch's conversion). Returns (q8, k8, v8, q_descale, k_descale, v_descale);
+    element x of q8 stands for q_descale * x."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed if seed is None else seed)
+    out = []
+    scales = []
+    for shape, dist in (((w.B, w.H, w.Nq, w.d), w.q_dist), ((w.B, w.H, w.Nk, w.d), w.k_dist),
+                        ((w.B, w.H, w.Nk, w.d), w.v_dist)):
+        x = _draw(g, shape, dist)
+        amax = float(x.abs().max())
+        s = torch.tensor(amax / FP8_MAX if amax > 0 else 1.0, dtype=torch.float32)
+        out.append((x / s).to(torch.float8_e4m3fn).contiguous())
+        scales.append(float(s))
+    return tuple(out) + tuple(scales)
+
+
+def dequantize_fp8(x8: torch.Tensor, descale: float) -> torch.Tensor:
+    """The values an e4m3 tensor stands for, exactly, in float64."""
+    return x8.to(torch.float64) * float(torch.tensor(descale, dtype=torch.float32))
+
+
 # Offset between a workload's input seed and the seed of its upstream gradient.
 GRAD_SEED_OFFSET = 500_000
 
