@@ -40,7 +40,7 @@ Variant make_variant(bool causal) {
 #define FA_TILES_D32 32, 64, 4, 2, 4, true
 #endif
 #ifndef FA_TILES_D64
-#define FA_TILES_D64 64, 64, 4, 1, 4, false
+#define FA_TILES_D64 64, 64, 4, 2, 4, false
 #endif
 #ifndef FA_TILES_D128
 #define FA_TILES_D128 128, 64, 8, 1, 4, false

@@ -136,8 +136,14 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // dK and dV for one block of 32*NW keys.
+// Waves per SIMD the dK/dV kernel is compiled for (register budget); a build
+// can override it with -DFA_BWD_DKDV_WAVES=n to compare.
+#ifndef FA_BWD_DKDV_WAVES
+#define FA_BWD_DKDV_WAVES 1
+#endif
+
 template <int D, int NW, int S, bool CAUSAL, typename T>
-__global__ __launch_bounds__(NW * 64) void fa_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(NW * 64, FA_BWD_DKDV_WAVES) void fa_bwd_dkdv_kernel(BwdParams p) {
   using M = Mma<T>;
   using vec = typename M::vec;
   constexpr int BM = 32;                     // query rows per tile
@@ -322,24 +328,24 @@ __global__ __launch_bounds__(NW * 64) void fa_bwd_dkdv_kernel(BwdParams p) {
       const vec a = *(const vec*)(dos + a_off[s]);
       dpa = M::run(a, vf[s], s == 0 ? f32x16{} : dpa);
     }
-    // LSE*log2(e) and D of the lane's queries 8a + 4half + 0..3
-    f32x4 lz[4], dz[4];
+    // P and dS in place of S and dP, four queries at a time: LSE*log2(e) and
+    // D of the lane's queries 8a + 4half + 0..3
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      lz[a] = *(const f32x4*)(ax + 8 * a + 4 * half);
-      dz[a] = *(const f32x4*)(ax + BM + 8 * a + 4 * half);
-    }
-    float pr[16], ds[16];
+      const f32x4 lz = *(const f32x4*)(ax + 8 * a + 4 * half);
+      const f32x4 dz = *(const f32x4*)(ax + BM + 8 * a + 4 * half);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, -lz[i >> 2][i & 3]));
-      if (MASK) {
-        const int qi = i0 + 8 * (i >> 2) + 4 * half + (i & 3);
-        const bool vis = key < Nk && (!CAUSAL || key <= qi);
-        pv = vis ? pv : 0.f;
+      for (int b = 0; b < 4; ++b) {
+        const int i = 4 * a + b;
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, -lz[b]));
+        if (MASK) {
+          const int qi = i0 + 8 * a + 4 * half + b;
+          const bool vis = key < Nk && (!CAUSAL || key <= qi);
+          pv = vis ? pv : 0.f;
+        }
+        sa[i] = pv;
+        dpa[i] = pv * (dpa[i] - dz[b]);
       }
-      pr[i] = pv;
-      ds[i] = pv * (dpa[i] - dz[i >> 2][i & 3]);
     }
     // P^T and dS^T as A operands: k-step c2 takes registers 8c2 .. 8c2+7.
     vec pa[2], da[2];
@@ -348,8 +354,8 @@ __global__ __launch_bounds__(NW * 64) void fa_bwd_dkdv_kernel(BwdParams p) {
       u32x4 wp, wd;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        wp[m] = __builtin_bit_cast(uint32_t, M::cvt(pr[8 * c2 + 2 * m], pr[8 * c2 + 2 * m + 1]));
-        wd[m] = __builtin_bit_cast(uint32_t, M::cvt(ds[8 * c2 + 2 * m], ds[8 * c2 + 2 * m + 1]));
+        wp[m] = __builtin_bit_cast(uint32_t, M::cvt(sa[8 * c2 + 2 * m], sa[8 * c2 + 2 * m + 1]));
+        wd[m] = __builtin_bit_cast(uint32_t, M::cvt(dpa[8 * c2 + 2 * m], dpa[8 * c2 + 2 * m + 1]));
       }
       pa[c2] = __builtin_bit_cast(vec, wp);
       da[c2] = __builtin_bit_cast(vec, wd);
