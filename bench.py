@@ -388,7 +388,8 @@ def _counter_rows(csv_dir: str, counter: str):
 
 
 def write_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str,
-                  copy_write_dir: str, copy_mib: int, command: str, bwd: bool = False):
+                  copy_write_dir: str, copy_mib: int, command: str, bwd: bool = False,
+                  fp8: bool = False):
     """Record HBM bytes per launch of the attention kernel (the forward, or
     with bwd the dK/dV kernel of the backward, keyed "bwd:<workload>") from
     rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch), each scaled by
@@ -398,7 +399,7 @@ def write_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir:
     known = copy_mib * (1 << 20)
     cf = [v for k, v in _counter_rows(copy_fetch_dir, "FETCH_SIZE") if "copyBuffer" in k or "copy" in k.lower()]
     cw = [v for k, v in _counter_rows(copy_write_dir, "WRITE_SIZE") if "copyBuffer" in k or "copy" in k.lower()]
-    kname = "fa_bwd_dkdv_kernel" if bwd else "fa_fwd_kernel"
+    kname = "fa_bwd_dkdv_kernel" if bwd else ("fa_fwd_fp8_kernel" if fp8 else "fa_fwd_kernel")
     kf = [v for k, v in _counter_rows(fetch_dir, "FETCH_SIZE") if kname in k]
     kw = [v for k, v in _counter_rows(write_dir, "WRITE_SIZE") if kname in k]
     if not (cf and cw and kf and kw):
@@ -412,14 +413,16 @@ def write_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir:
             rec = json.load(fh)
     except (OSError, ValueError):
         rec = {}
-    rec["about"] = ("HBM bytes per launch of fa_fwd_kernel (key: workload) and of "
-                    "fa_bwd_dkdv_kernel (key: bwd:workload) from rocprofv3 FETCH_SIZE and "
+    rec["about"] = ("HBM bytes per launch of fa_fwd_kernel (key: workload), of "
+                    "fa_bwd_dkdv_kernel (key: bwd:workload) and of fa_fwd_fp8_kernel (key: "
+                    "fp8:workload) from rocprofv3 FETCH_SIZE and "
                     "WRITE_SIZE (KiB per dispatch), scaled by the same counters on a plain "
                     "device copy of known size. Written by bench.py --write-traffic.")
-    key = f"bwd:{workload}" if bwd else workload
+    key = f"bwd:{workload}" if bwd else (f"fp8:{workload}" if fp8 else workload)
     rec.setdefault("workloads", {})[key] = {
         "kernel": kname,
-        "kernel_source_sha": kernel_source_hash(BWD_KERNEL_SOURCES if bwd else None),
+        "kernel_source_sha": kernel_source_hash(BWD_KERNEL_SOURCES if bwd else
+                                                (FP8_KERNEL_SOURCES if fp8 else None)),
         "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
         "hbm_bytes_per_launch": round(fetch + write),
         "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
@@ -463,7 +466,7 @@ def main(argv=None):
     if args.write_traffic:
         fd, wd, cfd, cwd, mib = args.write_traffic
         print(json.dumps(write_traffic(args.workload, fd, wd, cfd, cwd, int(mib), args.command,
-                                       bwd=args.which == "bwd")))
+                                       bwd=args.which == "bwd", fp8=args.fp8)))
         return 0
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
@@ -512,7 +515,7 @@ def main(argv=None):
             "us_per_call": round(ms * 1e3, 3),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_MFMA_FP8_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_FP8_TFLOPS, 4),
-                         "traffic": None},
+                         "traffic": measured_traffic(f"fp8:{w.name}", FP8_KERNEL_SOURCES)},
             "kernel_source_sha": kernel_source_hash(FP8_KERNEL_SOURCES),
         }
         print(json.dumps(line), flush=True)
