@@ -294,6 +294,38 @@ def bwd_record(w, ms: float, per: dict):
     }
 
 
+def short_stats(w, calls: int = 200):
+    """Latency-bound sizes: device time per call (HIP graph of 100 calls),
+    the eager rate, p50/p95 and relative spread of individually event-timed
+    calls, and the algorithmic HBM rate against the 8 TB/s peak."""
+    import statistics
+
+    import torch
+
+    import exact_attention_23_amd as fa
+
+    dev_us = time_graph(w)
+    eager_us = time_gpu(w, 100, 10, 100.0) * 1e3
+    dev = torch.device("cuda:0")
+    q, k, v, o = layout_inputs(w, "bhnd", dev)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(calls)]
+    for e0, e1 in evs:
+        e0.record()
+        fa.attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        e1.record()
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+    gbs = w.algorithmic_bytes() / (dev_us * 1e-6) / 1e9
+    return {"us_per_call_device": round(dev_us, 3), "us_per_call_eager": round(eager_us, 3),
+            "p50_us": round(t[len(t) // 2], 3), "p95_us": round(t[int(len(t) * 0.95)], 3),
+            "std_over_mean": round(statistics.pstdev(t) / statistics.fmean(t), 4),
+            "algorithmic_hbm_gbs": round(gbs, 1),
+            "hbm_peak_frac": round(gbs / PEAK_HBM_GBS, 5),
+            "tflops": round(w.flops() / (dev_us * 1e-6) / 1e12, 3)}
+
+
 def cpu_baseline_bwd(w, budget_s: float = 12.0):
     """The gradient oracle on whole heads of w until ~budget_s of CPU time."""
     import numpy as np
@@ -527,6 +559,10 @@ def main(argv=None):
         n400_us = time_graph(WORKLOADS["yolo20"])
         n400_eager_us = time_gpu(WORKLOADS["yolo20"], max(args.steps, 50), args.warmup,
                                  args.settle_ms) * 1e3
+    short = None
+    if not args.no_n400 and args.workload != "yolo20":
+        # the two latency-bound sizes (20x20 and 19x19 maps): HBM rate and latency spread
+        short = {n: short_stats(WORKLOADS[n]) for n in ("yolo20", "tail361")}
     traffic = measured_traffic(w.name)
     line = {
         "metric": METRIC,
@@ -551,6 +587,7 @@ def main(argv=None):
         # included), which is what a caller without graphs sees
         "us_per_call_n400": None if n400_us is None else round(n400_us, 3),
         "us_per_call_n400_eager": None if n400_eager_us is None else round(n400_eager_us, 3),
+        "short_sequences": short,
         "mfma_peak_frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),

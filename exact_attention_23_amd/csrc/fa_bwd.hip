@@ -30,11 +30,17 @@ struct BwdKernels {
 // instead (two per SIMD, each staged tile shared by twice as many waves), at
 // the price of a few spilled registers, which measured 29-30% faster. The
 // dQ ring has 3 stages at d = 128 to fit LDS.
+#ifndef FA_BWD_SA
+#define FA_BWD_SA 3
+#endif
+#ifndef FA_BWD_SB128
+#define FA_BWD_SB128 4
+#endif
 template <int D, bool C, typename T>
 BwdKernels make_bwd() {
-  constexpr int NWA = D == 128 ? 8 : 4, SA = 3;
+  constexpr int NWA = D == 128 ? 8 : 4, SA = FA_BWD_SA;
   constexpr int NWB = D == 128 ? 8 : 4;
-  constexpr int SB = D == 128 ? 3 : 4;
+  constexpr int SB = D == 128 ? FA_BWD_SB128 : 4;
   return {fa::fa_bwd_pre_kernel<D, T>,
           fa::fa_bwd_dkdv_kernel<D, NWA, SA, C, T>,
           fa::fa_bwd_dq_kernel<D, NWB, SB, C, T>,
