@@ -136,6 +136,11 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // dK and dV for one block of 32*NW keys.
+// K rows of the dK/dV kernel in LDS at d = 128 (1) or in VGPRs (0).
+#ifndef FA_BWD_K_LDS
+#define FA_BWD_K_LDS 1
+#endif
+
 // Waves per SIMD the dK/dV kernel is compiled for (register budget); a build
 // can override it with -DFA_BWD_DKDV_WAVES=n to compare.
 #ifndef FA_BWD_DKDV_WAVES
@@ -172,6 +177,10 @@ __global__ __launch_bounds__(NW * 64, FA_BWD_DKDV_WAVES) void fa_bwd_dkdv_kernel
   __shared__ __attribute__((aligned(1024))) char ring[S][2][TILE];
   __shared__ __attribute__((aligned(1024))) char trb[2][2][TILE];
   __shared__ __attribute__((aligned(16))) float auxs[S][2 * BM];
+  // At d = 128 the wave's K rows live in LDS instead of VGPRs (the registers
+  // are full there); each wave reads back only its own 32 rows.
+  constexpr bool K_LDS = FA_BWD_K_LDS && D == 128;
+  __shared__ __attribute__((aligned(1024))) char kls[K_LDS ? 32 * NW : 1][K_LDS ? 2 * D : 16];
 
   int head, kb;
   bwd_work_item<false>(p, blockIdx.x, head, kb);
@@ -201,11 +210,18 @@ __global__ __launch_bounds__(NW * 64, FA_BWD_DKDV_WAVES) void fa_bwd_dkdv_kernel
   const int key = kw0 + r32;       // this lane's key (keys past Nk read as zero)
 
   // K and V rows of the lane's key: B operands of S = Q K^T and dP = dO V^T.
-  vec kf[KS], vf[KS];
+  vec kf[K_LDS ? 1 : KS], vf[KS];
+  int k_off[K_LDS ? KS : 1];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     const int off = key * (2 * D) + 2 * (16 * s + 8 * half);
-    kf[s] = __builtin_bit_cast(vec, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, off, 0, 0));
+    const vec kv = __builtin_bit_cast(vec, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, off, 0, 0));
+    if constexpr (K_LDS) {
+      k_off[s] = lds_off<2 * D>(32 * wave + r32, 2 * s + half);
+      *(vec*)(&kls[0][0] + k_off[s]) = kv;  // read back by this lane only
+    } else {
+      kf[s] = kv;
+    }
     vf[s] = __builtin_bit_cast(vec, __builtin_amdgcn_raw_buffer_load_b128(v_rsrc, off, 0, 0));
   }
 
@@ -321,7 +337,12 @@ __global__ __launch_bounds__(NW * 64, FA_BWD_DKDV_WAVES) void fa_bwd_dkdv_kernel
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const vec a = *(const vec*)(qs + a_off[s]);
-      sa = M::run(a, kf[s], s == 0 ? f32x16{} : sa);
+      vec kb;
+      if constexpr (K_LDS)
+        kb = *(const vec*)(&kls[0][0] + k_off[s]);
+      else
+        kb = kf[s];
+      sa = M::run(a, kb, s == 0 ? f32x16{} : sa);
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {

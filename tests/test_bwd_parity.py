@@ -185,3 +185,74 @@ def test_bwd_named_workload_full_size(name):
     for (b, h) in heads:
         ref = oracle.attention_backward_head(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal)
         compare_grads(tuple(g[b, h] for g in got), ref, q.dtype, what=f"{name} head ({b},{h})")
+
+
+def _raw_bwd_args(q, k, v, o, do, lse, dq, dk, dv, ws, causal, scale):
+    B, H, Nq, d = q.shape
+    return (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
+            B, H, Nq, k.shape[2], d, float(scale), 1 if causal else 0, fa._dtype_code(q))
+
+
+def test_bwd_kernels_on_two_streams():
+    """The documented split: FA_BWD_PRE, then FA_BWD_DKDV and FA_BWD_DQ on two
+    streams that both wait for it, gives the bits of one fa_bwd call."""
+    require_gpu()
+    note("bwd two streams")
+    from exact_attention_23_amd import _lib
+
+    dev = torch.device("cuda:0")
+    for d, dt in ((64, "fp16"), (128, "bf16")):
+        q, k, v = (t.to(dev) for t in rand_inputs(2, 3, 333, 517, d, dt, seed=d + 9))
+        do = grad_like(q.cpu(), seed=d + 10).to(dev)
+        o, lse = fa.attention(q, k, v, causal=True)
+        ref = fa.attention_backward(q, k, v, o, do, lse, causal=True)
+        dq, dk, dv = (torch.full_like(t, float("nan")) for t in (q, k, v))
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(2, 3, 333), dtype=torch.uint8, device=dev)
+        args = _raw_bwd_args(q, k, v, o, do, lse, dq, dk, dv, ws, True, default_scale(d))
+        lib = _lib.load()
+        main = torch.cuda.current_stream()
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        assert lib.fa_bwd_ex(*args, _lib.FA_BWD_PRE, main.cuda_stream) == 0
+        s1.wait_stream(main)
+        s2.wait_stream(main)
+        assert lib.fa_bwd_ex(*args, _lib.FA_BWD_DKDV, s1.cuda_stream) == 0
+        assert lib.fa_bwd_ex(*args, _lib.FA_BWD_DQ, s2.cuda_stream) == 0
+        main.wait_stream(s1)
+        main.wait_stream(s2)
+        torch.cuda.synchronize()
+        for x, y, n in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+            assert torch.equal(x, y), f"d={d}: {n} differs from one fa_bwd call"
+
+
+def test_bwd_graph_replay_matches_eager():
+    """The backward captured in a HIP graph gives the eager bits on every
+    replay, with eager work and synchronisation between replays."""
+    require_gpu()
+    note("bwd graph replay")
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in rand_inputs(2, 2, 300, 400, 64, "fp16", seed=21))
+    do = grad_like(q.cpu(), seed=22).to(dev)
+    o, lse = fa.attention(q, k, v, causal=True)
+    ref = fa.attention_backward(q, k, v, o, do, lse, causal=True)
+    dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fa.attention_backward(q, k, v, o, do, lse, causal=True, dq=dq, dk=dk, dv=dv)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(2):
+            fa.attention_backward(q, k, v, o, do, lse, causal=True, dq=dq, dk=dk, dv=dv)
+    for rep in range(4):
+        for t in (dq, dk, dv):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for x, y, n in zip((dq, dk, dv), ref, ("dq", "dk", "dv")):
+            assert torch.equal(x, y), f"replay {rep}: {n} differs"
+        fa.attention_backward(q, k, v, o, do, lse, causal=False)  # eager work between replays
+        torch.cuda.synchronize()
