@@ -18,7 +18,22 @@ from ._lib import (FA_DTYPE_BF16, FA_DTYPE_FP16, FA_OK, FA_PATH_AUTO,  # noqa: F
 __all__ = ["FaError", "fa_fwd", "fa_fwd_ex", "fa_fwd_strided", "attention_fp8", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_bytes", "attention",
            "attention_backward", "flash_attention", "version"]
 
-_PATHS = {"auto": FA_PATH_AUTO, "tiled": FA_PATH_TILED, "short": FA_PATH_SHORT}
+_PATHS = {"auto": FA_PATH_AUTO, "tiled": FA_PATH_TILED, "short": FA_PATH_SHORT, "stream": -1}
+
+# Workspaces of the stream form, one per (device, stream): calls on one stream
+# run in order, so they can share it.
+_STREAM_WS = {}
+
+
+def _stream_workspace(device, stream, nbytes):
+    import torch
+
+    key = (device.index, stream)
+    ws = _STREAM_WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _STREAM_WS[key] = ws
+    return ws
 
 
 class FaError(RuntimeError):
@@ -167,7 +182,16 @@ def attention(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
             lse.data_ptr() if lse is not None else None, B, H, Nq, Nk, d)
     tail = (float(scale), 1 if causal else 0, code)
-    if contiguous:
+    use_stream = contiguous and (path == "stream" or (
+        path == "auto" and lib.fa_fwd_stream_advised(B, H, Nq, Nk, d, code, 1 if causal else 0)))
+    if use_stream:
+        st_handle = _current_stream(q.device.index)
+        nbytes = lib.fa_fwd_stream_workspace_bytes(B, H, Nq, Nk, d, code)
+        if nbytes < 0:
+            raise FaError(_lib.FA_ERR_LAUNCH, "stream form unavailable on this device")
+        ws = _stream_workspace(q.device, st_handle, nbytes)
+        fn, call = lib.fa_fwd_stream, ptrs + tail[:1] + (tail[1], code, ws.data_ptr(), ws.numel())
+    elif contiguous:
         fn, call = lib.fa_fwd_ex, ptrs + tail + (_PATHS[path],)
     else:
         if path != "auto":

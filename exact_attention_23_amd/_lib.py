@@ -66,6 +66,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp,
                                    ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
     lib.fa_fwd_strided.restype = ctypes.c_int
+    lib.fa_fwd_stream_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int]
+    lib.fa_fwd_stream_workspace_bytes.restype = i64
+    lib.fa_fwd_stream_advised.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.fa_fwd_stream_advised.restype = ctypes.c_int
+    lib.fa_fwd_stream.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                                  ctypes.c_int, ctypes.c_int, vp, i64, vp]
+    lib.fa_fwd_stream.restype = ctypes.c_int
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                                ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int,
                                ctypes.c_int, vp]

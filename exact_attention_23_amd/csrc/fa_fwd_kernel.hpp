@@ -124,8 +124,15 @@ __device__ __forceinline__ void work_item(const Params& p, int bid, int& head, i
   qb = CAUSAL ? (p.num_qb - 1 - rank) : rank;
 }
 
+// One query block (head, qb) over key tiles [t_lo, t_hi) (clipped to the
+// tiles the block sees). part == nullptr: the block's whole key range, so O
+// and LSE are written. Otherwise a piece of it: the unnormalised O^T
+// ([D][BM] fp32), the reference maximum and the row sum (each [BM] fp32)
+// go to part, to be merged with the block's other pieces.
 template <int D, int BN, int NW, int RB, int S, bool PIPE, bool CAUSAL, typename T>
-__global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
+__device__ __forceinline__ void fa_fwd_block(const Params& p, int head, int qb, int t_lo, int t_hi,
+                                             float* part, char (&smem)[S][2][BN * D * 2],
+                                             char (&vts)[2][BN * D * 2]) {
   using M = Mma<T>;
   using vec = typename M::vec;
   using pair = typename M::pair;
@@ -150,14 +157,6 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   constexpr int PENDING = (S - 3) * LOADS;
   static_assert(S >= 3 && PENDING < 64, "stage count out of range");
 
-  // K and V tiles as loaded ([stage][K,V], rows = keys), and V^T tiles
-  // (rows = d, BN keys each) for the P V operand, double-buffered: while
-  // tile j runs, V^T of tile j+1 is written.
-  __shared__ __attribute__((aligned(1024))) char smem[S][2][TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vts[2][TILE_BYTES];
-
-  int head, qb;
-  work_item<CAUSAL>(p, blockIdx.x, head, qb);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -201,6 +200,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
     kv_end = last < Nk ? last : Nk;
   }
   const int ntiles = (kv_end + BN - 1) / BN;
+  t_hi = t_hi < ntiles ? t_hi : ntiles;  // tiles of this call: [t_lo, t_hi)
 
   f32x16 oacc[RB][NDT];
 #pragma unroll
@@ -249,9 +249,9 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   // those loads only write zeros to LDS and touch no memory.
   constexpr uint32_t kOutOfRange = 0x40000000u;
   auto issue = [&](int t) {
-    const int st = t % S;
-    const uint32_t kbase = t < ntiles ? (uint32_t)(t * BN * krs) : kOutOfRange;
-    const uint32_t vbase = t < ntiles ? (uint32_t)(t * BN * vrs) : kOutOfRange;
+    const int st = (t - t_lo) % S;
+    const uint32_t kbase = t < t_hi ? (uint32_t)(t * BN * krs) : kOutOfRange;
+    const uint32_t vbase = t < t_hi ? (uint32_t)(t * BN * vrs) : kOutOfRange;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const uint32_t blk = (uint32_t)((wave * CPT + i) * 1024);
@@ -297,8 +297,8 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
 
   // V tile j (as loaded) -> V^T buffer j % 2
   auto transpose_v = [&](int j) {
-    const char* vsrc = smem[j % S][1];
-    char* vdst = vts[j & 1];
+    const char* vsrc = smem[(j - t_lo) % S][1];
+    char* vdst = vts[(j - t_lo) & 1];
     i16x4 blk[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i)
@@ -327,12 +327,12 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   // S^T = K Q^T, one per k-step) and V^T of subtile t of tile j (A operands
   // of O^T += V^T P^T, per 16-key half s2 and 32-wide d tile).
   auto load_k = [&](int j, int t, vec (&kf)[KS]) {
-    const char* ks = smem[j % S][0];
+    const char* ks = smem[(j - t_lo) % S][0];
 #pragma unroll
     for (int s = 0; s < KS; ++s) kf[s] = *(const vec*)(ks + k_roff[t][s]);
   };
   auto load_v = [&](int j, int t, vec (&vf)[2][NDT]) {
-    const char* vs = vts[j & 1];
+    const char* vs = vts[(j - t_lo) & 1];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
     {
       // k-step outer, unit inner: consecutive MFMAs feed different
       // accumulators
-      const char* ks = smem[j % S][0];
+      const char* ks = smem[(j - t_lo) % S][0];
 #pragma unroll
       for (int s = 0; s < KS; ++s)
 #pragma unroll
@@ -577,43 +577,63 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
     tile_end();
   };
 
-  // ---- prologue: tiles 0..S-2 requested, V^T of tile 0 written.
+  // ---- prologue: tiles t_lo..t_lo+S-2 requested, V^T of tile t_lo written.
 #pragma unroll
-  for (int t = 0; t < S - 1; ++t) issue(t);
+  for (int t = 0; t < S - 1; ++t) issue(t_lo + t);
   wait_vmcnt<PENDING>();
   __syncthreads();
-  transpose_v(0);
+  transpose_v(t_lo);
   __syncthreads();
 
   const auto unmasked = std::integral_constant<bool, false>{};
   const auto masked = std::integral_constant<bool, true>{};
-  int j = 0;
+  const int j_free = first_masked < t_hi ? first_masked : t_hi;
+  int j = t_lo;
   if constexpr (PIPE) {
-    // Scores of unit (0, 0) before the loop; the first unit's test raises
-    // the reference from -inf.
+    // Scores of the first unit before the loop; its test raises the
+    // reference from -inf.
     {
       vec kf[KS];
-      load_k(0, 0, kf);
+      load_k(t_lo, 0, kf);
       qk(kf, sacc[0]);
     }
-    for (; j < first_masked; ++j) {
+    for (; j < j_free; ++j) {
       tile_start(j);
       piped_tile(unmasked, j);
     }
-    for (; j < ntiles; ++j) {
+    for (; j < t_hi; ++j) {
       tile_start(j);
       piped_tile(masked, j);
     }
   }
   if constexpr (!PIPE) {
-    for (; j < first_masked; ++j) {
+    for (; j < j_free; ++j) {
       tile_start(j);
       plain_tile(unmasked, j);
     }
-    for (; j < ntiles; ++j) {
+    for (; j < t_hi; ++j) {
       tile_start(j);
       plain_tile(masked, j);
     }
+  }
+
+  if (part != nullptr) {
+    // ---- a piece of the key range: unnormalised O^T, reference, row sum
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int row = wave * WR + 32 * rb + r32;  // row within the block
+      const float l_tot = M::kMfmaRowSum ? l_run[rb] : sum_with_partner(l_run[rb]);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          part[(32 * dt + 8 * (i >> 2) + 4 * half + (i & 3)) * BM + row] = oacc[rb][dt][i];
+      if (half == 0) {
+        part[D * BM + row] = m_run[rb];
+        part[D * BM + BM + row] = l_tot;
+      }
+    }
+    return;
   }
 
   // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
@@ -639,6 +659,18 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
         p.lse[(size_t)head * Nq + q_row] = 0.69314718055994531f * (m_run[rb] + log2f(l_tot));
     }
   }
+}
+
+template <int D, int BN, int NW, int RB, int S, bool PIPE, bool CAUSAL, typename T>
+__global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
+  // K and V tiles as loaded ([stage][K,V], rows = keys), and V^T tiles
+  // (rows = d, BN keys each) for the P V operand, double-buffered: while
+  // tile j runs, V^T of tile j+1 is written.
+  __shared__ __attribute__((aligned(1024))) char smem[S][2][BN * D * 2];
+  __shared__ __attribute__((aligned(1024))) char vts[2][BN * D * 2];
+  int head, qb;
+  work_item<CAUSAL>(p, blockIdx.x, head, qb);
+  fa_fwd_block<D, BN, NW, RB, S, PIPE, CAUSAL, T>(p, head, qb, 0, 0x7fffffff, nullptr, smem, vts);
 }
 
 }  // namespace fa

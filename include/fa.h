@@ -152,6 +152,42 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
                    const int64_t* strides, float scale, int causal, int dtype, void* stream);
 
 /*
+ * Persistent ("stream") form of the forward, for full masks. fa_fwd gives
+ * every workgroup one block of query rows; when the blocks outnumber the
+ * workgroups the GPU holds at once by a non-integer factor, the last round
+ * runs partly empty. fa_fwd_stream launches exactly the resident workgroups
+ * and gives each an equal share of the (query block, key tile) work; a query
+ * block whose key range is cut between two workgroups is computed in pieces
+ * (each with its own running maximum, sum and output, as in the online
+ * softmax of the kwkr.cn YOLO11 FlashAttention-2 article, section 1.2) and a
+ * second kernel merges the pieces exactly.
+ *
+ * fa_fwd_stream_workspace_bytes - workspace bytes fa_fwd_stream needs on the
+ * current device for these sizes (it depends on how many workgroups the
+ * device holds at once); -1 for invalid arguments or a failed device query.
+ *
+ * fa_fwd_stream_advised - 1 when the stream form is expected to beat fa_fwd
+ * for these arguments on the current device: full mask, and query blocks
+ * filling one or two rounds of the resident workgroups plus at most a
+ * quarter of another (fa_fwd then runs a mostly empty last round); else 0.
+ * Never fails.
+ *
+ * fa_fwd_stream - fa_fwd (contiguous tensors, same arguments, results and
+ * checks) on the stream form. causal = 1 returns FA_ERR_PATH. workspace:
+ * device memory of at least fa_fwd_stream_workspace_bytes bytes, 16-byte
+ * aligned, caller-owned, not overlapping any tensor (FA_ERR_WORKSPACE,
+ * FA_ERR_ALIAS); its contents on entry do not matter. Two kernels are
+ * enqueued on `stream`. Deterministic (fixed split and merge order).
+ */
+int64_t fa_fwd_stream_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                      int dtype);
+int fa_fwd_stream_advised(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype,
+                          int causal);
+int fa_fwd_stream(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+                  int dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * fa_fwd_fp8 - exact attention forward on FP8 inputs (FlashAttention-3's FP8
  * variant, ai2ai.xin flash-attention-principle page, FA-3 section).
  *

@@ -315,3 +315,34 @@ def fcall(**kw):
 ])
 def test_fp8_invalid_arguments_rejected_before_launch(kw, status):
     assert fcall(**kw) == status
+
+
+# ---- stream forward
+def stcall(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    ws = a.get("ws", WS)
+    return _lib.load().fa_fwd_stream(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                     a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"],
+                                     ws, a.get("ws_bytes", 1 << 30), a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), _lib.FA_ERR_NULLPTR),
+    (dict(d=96), _lib.FA_ERR_HEADDIM),
+    (dict(causal=1), _lib.FA_ERR_PATH),
+    (dict(ws=0), _lib.FA_ERR_WORKSPACE),
+    (dict(ws=WS + 4), _lib.FA_ERR_WORKSPACE),
+    (dict(o=Q), _lib.FA_ERR_ALIAS),
+])
+def test_stream_invalid_arguments_rejected_before_launch(kw, status):
+    assert stcall(**kw) == status
+
+
+def test_stream_size_queries_reject_bad_sizes():
+    lib = _lib.load()
+    assert lib.fa_fwd_stream_workspace_bytes(0, 1, 1, 1, 64, 0) == -1
+    assert lib.fa_fwd_stream_workspace_bytes(1, 1, 1, 1, 96, 0) == -1
+    assert lib.fa_fwd_stream_workspace_bytes(1, 1, 1, 1, 64, 3) == -1
+    assert lib.fa_fwd_stream_advised(16, 4, 6400, 6400, 32, 0, 1) == 0  # causal
+    assert lib.fa_fwd_stream_advised(0, 4, 6400, 6400, 32, 0, 0) == 0
