@@ -25,5 +25,6 @@ from .definition import (  # noqa: F401
 from .backward import (  # noqa: F401
     attention_backward_head,
     attention_backward,
+    attention_backward_sampled,
     row_delta,
 )

@@ -87,3 +87,39 @@ def row_delta(o, do) -> np.ndarray:
     """D_i = sum_d dO_id O_id per query row ([B, H, Nq] float64). Equal to
     sum_j P_ij dP_ij of attention_backward_head, since O_i = sum_j P_ij V_j."""
     return (to_f64(o) * to_f64(do)).sum(axis=-1)
+
+
+def attention_backward_sampled(q_h, k_h, v_h, do_h, scale: float, causal: bool = False,
+                               rows=(), keys=(), row_block: int = 1024):
+    """dQ for selected query rows and dK, dV for selected keys of one head,
+    for heads too long to hold S whole.
+
+    The same chain rule as attention_backward_head, with the query rows taken
+    row_block at a time: each row's P, dP and D depend on that row alone, so
+    dQ of a row comes from its own block, and dK_j, dV_j (sums over all rows
+    i) are accumulated block by block. Returns (dQ [len(rows), d],
+    dK [len(keys), d], dV [len(keys), d])."""
+    q_h, k_h, v_h, do_h = to_f64(q_h), to_f64(k_h), to_f64(v_h), to_f64(do_h)
+    _check_head_shapes(q_h, k_h, v_h)
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    Nq, d = q_h.shape
+    dQ = np.zeros((len(rows), d))
+    dK = np.zeros((len(keys), d))
+    dV = np.zeros((len(keys), d))
+    for r0 in range(0, Nq, row_block):
+        r1 = min(Nq, r0 + row_block)
+        S = scores(q_h[r0:r1], k_h, scale)
+        if causal:
+            S = apply_causal_mask(S, np.arange(r0, r1))
+        E, _, l = softmax_stats(S)
+        P = E / l[:, None]
+        dP = do_h[r0:r1] @ v_h.T
+        D = (P * dP).sum(axis=1)
+        dS = P * (dP - D[:, None])
+        dV += P[:, keys].T @ do_h[r0:r1]
+        dK += scale * (dS[:, keys].T @ q_h[r0:r1])
+        sel = (rows >= r0) & (rows < r1)
+        if sel.any():
+            dQ[sel] = scale * (dS[rows[sel] - r0] @ k_h)
+    return dQ, dK, dV

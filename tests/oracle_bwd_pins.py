@@ -175,6 +175,22 @@ def check_default_scale(ora):
         _close(dV, tv.grad.numpy(), 1e-11, f"default scale dV causal={causal}")
 
 
+def check_sampled_matches_full(ora):
+    """The row-blocked sampled form against the whole-head gradients."""
+    rng = np.random.default_rng(21)
+    for causal, (Nq, Nk, d, blk) in ((False, (37, 29, 8, 10)), (True, (40, 40, 6, 7)),
+                                     (True, (25, 60, 4, 100))):
+        q, k, v, do = _inputs(rng, 1, 1, Nq, Nk, d, sigma=1.3)
+        full = ora.attention_backward_head(q[0, 0], k[0, 0], v[0, 0], do[0, 0], 0.45, causal)
+        rows = [0, 3, Nq // 2, Nq - 1]
+        keys = [0, 1, Nk // 3, Nk - 1]
+        dq, dk, dv = ora.attention_backward_sampled(q[0, 0], k[0, 0], v[0, 0], do[0, 0], 0.45,
+                                                    causal, rows, keys, row_block=blk)
+        _close(dq, full[0][rows], 1e-12, f"sampled dQ causal={causal}")
+        _close(dk, full[1][keys], 1e-12, f"sampled dK causal={causal}")
+        _close(dv, full[2][keys], 1e-12, f"sampled dV causal={causal}")
+
+
 ALL_CHECKS = [
     check_finite_differences,
     check_torch_autograd,
@@ -186,4 +202,5 @@ ALL_CHECKS = [
     check_linear_in_do,
     check_row_delta,
     check_default_scale,
+    check_sampled_matches_full,
 ]

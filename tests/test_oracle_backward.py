@@ -26,7 +26,7 @@ MUTANTS = [
     ("dv_untransposed", "dV = P.T @ do_h", "dV = P @ do_h"),
     ("dv_from_scores", "dV = P.T @ do_h", "dV = E.T @ do_h"),
     ("dp_with_keys", "dP = do_h @ v_h.T", "dP = do_h @ k_h.T"),
-    ("delta_over_columns", "D = (P * dP).sum(axis=1)", "D = (P * dP).sum(axis=0)"),
+    ("delta_over_columns", "    D = (P * dP).sum(axis=1)\n    dS", "    D = (P * dP).sum(axis=0)\n    dS"),
     ("delta_dropped", DS_LINE, "dS = P * dP\n    dQ"),
     ("delta_sign", DS_LINE, "dS = P * (dP + D[:, None])\n    dQ"),
     ("ds_without_p", DS_LINE, "dS = (dP - D[:, None])\n    dQ"),
@@ -36,7 +36,13 @@ MUTANTS = [
     ("dk_from_do", "dK = scale * (dS.T @ q_h)", "dK = scale * (dS.T @ do_h)"),
     ("no_causal_mask", "        S = apply_causal_mask(S, np.asarray(row_ids))",
      "        S = S"),
-    ("unnormalised_p", "P = E / l[:, None]", "P = E"),
+    ("unnormalised_p", "    P = E / l[:, None]\n    dV", "    P = E\n    dV"),
+    # the row-blocked sampled form
+    ("sampled_dv_overwritten", "dV += P[:, keys].T @ do_h[r0:r1]", "dV = P[:, keys].T @ do_h[r0:r1]"),
+    ("sampled_mask_block_local", "S = apply_causal_mask(S, np.arange(r0, r1))",
+     "S = apply_causal_mask(S, np.arange(0, r1 - r0))"),
+    ("sampled_row_selection", "sel = (rows >= r0) & (rows < r1)", "sel = (rows > r0) & (rows < r1)"),
+    ("sampled_dk_no_scale", "dK += scale * (dS[:, keys].T @ q_h[r0:r1])", "dK += dS[:, keys].T @ q_h[r0:r1]"),
     ("row_delta_wrong_axis", "return (to_f64(o) * to_f64(do)).sum(axis=-1)",
      "return (to_f64(o) * to_f64(do)).sum(axis=-2)"),
     ("default_scale_wrong", "scale = 1.0 / math.sqrt(d)\n    dQ", "scale = 1.0 / d\n    dQ"),
