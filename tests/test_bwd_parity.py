@@ -256,3 +256,26 @@ def test_bwd_graph_replay_matches_eager():
             assert torch.equal(x, y), f"replay {rep}: {n} differs"
         fa.attention_backward(q, k, v, o, do, lse, causal=False)  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_bwd_long16k_full_size_sampled():
+    """The 16384-token causal bf16 workload at full size (the d = 128
+    backward kernels: 8-wave workgroups, K rows in LDS): dQ of sampled rows
+    and dK, dV of sampled keys of one head, from the row-blocked gradient
+    oracle (tens of seconds of CPU)."""
+    require_gpu()
+    w = WORKLOADS["long16k"]
+    note(f"bwd parity workload long16k: B={w.B} H={w.H} N={w.Nq} d={w.d} {w.dtype} causal={w.causal}")
+    q, k, v = make_inputs(w)
+    do = make_grad(w)
+    got = run_bwd(q, k, v, do, w.causal, w.scale)
+    for g in got:
+        assert torch.isfinite(g.float()).all()
+    rng = np.random.default_rng(w.seed)
+    picks = sorted(set([0, 1, 63, 64, 255, 256, 8191, 16382, 16383] +
+                       [int(x) for x in rng.integers(0, w.Nq, 24)]))
+    for h in (w.H - 1,):
+        dq, dk, dv = oracle.attention_backward_sampled(q[0, h], k[0, h], v[0, h], do[0, h], w.scale,
+                                                       w.causal, picks, picks, row_block=2048)
+        compare_grads((got[0][0, h][picks], got[1][0, h][picks], got[2][0, h][picks]),
+                      (dq, dk, dv), q.dtype, what=f"long16k head {h}")
