@@ -585,6 +585,11 @@ __device__ __forceinline__ void fa_fwd_block(const Params& p, int head, int qb, 
   transpose_v(t_lo);
   __syncthreads();
 
+  // Causal: a tile whose first key comes after this wave's last row adds
+  // nothing to any of its rows, and neither does any later tile. The test is
+  // wave-uniform; the scores a pipelined wave carries into such a tile are
+  // never used.
+  auto beyond_rows = [&](int j) { return CAUSAL && j * BN > wave_q0 + WR - 1; };
   const auto unmasked = std::integral_constant<bool, false>{};
   const auto masked = std::integral_constant<bool, true>{};
   const int j_free = first_masked < t_hi ? first_masked : t_hi;
@@ -601,7 +606,7 @@ __device__ __forceinline__ void fa_fwd_block(const Params& p, int head, int qb, 
       tile_start(j);
       piped_tile(unmasked, j);
     }
-    for (; j < t_hi; ++j) {
+    for (; j < t_hi && !beyond_rows(j); ++j) {
       tile_start(j);
       piped_tile(masked, j);
     }
@@ -611,10 +616,17 @@ __device__ __forceinline__ void fa_fwd_block(const Params& p, int head, int qb, 
       tile_start(j);
       plain_tile(unmasked, j);
     }
-    for (; j < t_hi; ++j) {
+    for (; j < t_hi && !beyond_rows(j); ++j) {
       tile_start(j);
       plain_tile(masked, j);
     }
+  }
+
+  // Causal tiles past this wave's rows: only its share of the loads,
+  // transposes and barriers.
+  for (; j < t_hi; ++j) {
+    tile_start(j);
+    tile_end();
   }
 
   if (part != nullptr) {
@@ -661,8 +673,15 @@ __device__ __forceinline__ void fa_fwd_block(const Params& p, int head, int qb, 
   }
 }
 
+// Waves per SIMD the register allocation must allow. At d = 64 two
+// workgroups share a CU by LDS (80 KB each), and the bf16 form (fp32 row
+// sums on the vector units) would otherwise take a few registers more than
+// half the file and run one wave per SIMD; capped, it spills about a dozen
+// registers and runs 15% faster.
+constexpr int fwd_min_waves(int d) { return d == 64 ? 2 : 1; }
+
 template <int D, int BN, int NW, int RB, int S, bool PIPE, bool CAUSAL, typename T>
-__global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
+__global__ __launch_bounds__(NW * 64, fwd_min_waves(D)) void fa_fwd_kernel(Params p) {
   // K and V tiles as loaded ([stage][K,V], rows = keys), and V^T tiles
   // (rows = d, BN keys each) for the P V operand, double-buffered: while
   // tile j runs, V^T of tile j+1 is written.
