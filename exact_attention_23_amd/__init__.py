@@ -25,6 +25,21 @@ _PATHS = {"auto": FA_PATH_AUTO, "tiled": FA_PATH_TILED, "short": FA_PATH_SHORT, 
 _STREAM_WS = {}
 
 
+_ADVISED = {}
+
+
+def _stream_advised(lib, device_index, *shape) -> bool:
+    """fa_fwd_stream_advised for one device and call shape, asked once (a
+    ctypes call costs about a microsecond on every attention() call)."""
+    key = (device_index,) + shape
+    r = _ADVISED.get(key)
+    if r is None:
+        r = bool(lib.fa_fwd_stream_advised(*shape))
+        if len(_ADVISED) < 4096:
+            _ADVISED[key] = r
+    return r
+
+
 def _stream_workspace(device, stream, nbytes):
     import torch
 
@@ -183,7 +198,8 @@ def attention(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
             lse.data_ptr() if lse is not None else None, B, H, Nq, Nk, d)
     tail = (float(scale), 1 if causal else 0, code)
     use_stream = contiguous and (path == "stream" or (
-        path == "auto" and lib.fa_fwd_stream_advised(B, H, Nq, Nk, d, code, 1 if causal else 0)))
+        path == "auto" and _stream_advised(lib, q.device.index, B, H, Nq, Nk, d, code,
+                                           1 if causal else 0)))
     if use_stream:
         st_handle = _current_stream(q.device.index)
         nbytes = lib.fa_fwd_stream_workspace_bytes(B, H, Nq, Nk, d, code)

@@ -284,10 +284,20 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_fp8_kernel(Fp8Params pp) {
     wait_vmcnt<PENDING>();
     __syncthreads();
   }
-  for (; j < ntiles; ++j) {
+  // Causal: tiles whose first key comes after this wave's last row add
+  // nothing to its rows; the wave only takes its share of their loads,
+  // transposes and barriers.
+  const int wave_last_row = qb * BM + 32 * wave + 31;
+  for (; j < ntiles && !(CAUSAL && j * BN > wave_last_row); ++j) {
     issue(j + S - 1);
     transpose_v(j + 1);
     tile(masked, j);
+    wait_vmcnt<PENDING>();
+    __syncthreads();
+  }
+  for (; j < ntiles; ++j) {
+    issue(j + S - 1);
+    transpose_v(j + 1);
     wait_vmcnt<PENDING>();
     __syncthreads();
   }

@@ -44,11 +44,11 @@ __global__ __launch_bounds__(1024) void fa_fwd_short_kernel(Params p) {
   constexpr int NDT = D / 32;   // 32-wide d tiles of O
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   constexpr int MAXW = kShortMaxWaves<D>;
-  constexpr int PS = D + 4;                 // floats per row of a partial O (padded)
+  constexpr int PS = D + 4;                 // floats per row of a partial O (padded; rows stay 16-byte aligned)
   constexpr int REGION = 32 * PS * 4;       // per-wave LDS bytes: partial O ...
   static_assert(REGION >= 64 * D * 2, "... and, before it, the wave's V tile");
   __shared__ __attribute__((aligned(1024))) char smem[MAXW * REGION];
-  __shared__ float s_m[MAXW][32], s_l[MAXW][32], s_M[32], s_L[32];
+  __shared__ float s_m[MAXW][32], s_l[MAXW][32];
 
   const int head = blockIdx.x / p.num_qb;
   const int qb = blockIdx.x - head * p.num_qb;
@@ -88,27 +88,34 @@ __global__ __launch_bounds__(1024) void fa_fwd_short_kernel(Params p) {
     }
   }
 
-  // ---- Q rows (B operands) and K rows (A operands, permuted key order)
-  vec qf[KS];
+  // ---- Q rows (B operands) and K rows (A operands, permuted key order).
+  // Every load is issued before the first is used, so the chain pays one
+  // memory round trip, not one per k-step.
+  u32x4 qw[KS], kw[2][KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, q_row * qrs + 2 * (16 * s + 8 * half),
-                                                    0, 0);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = (w[e] & p.q_and) ^ p.q_xor;
-    qf[s] = __builtin_bit_cast(vec, w);
-  }
-  f32x16 sacc[2];
+  for (int s = 0; s < KS; ++s)
+    qw[s] = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, q_row * qrs + 2 * (16 * s + 8 * half), 0, 0);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int krow = kb + 32 * t + lds_row_to_key(r32);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const vec a = __builtin_bit_cast(
-          vec, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, krow * krs + 2 * (16 * s + 8 * half), 0, 0));
-      sacc[t] = M::run(a, qf[s], s == 0 ? f32x16{} : sacc[t]);
-    }
+    for (int s = 0; s < KS; ++s)
+      kw[t][s] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, krow * krs + 2 * (16 * s + 8 * half), 0, 0);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  vec qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qw[s][e] = (qw[s][e] & p.q_and) ^ p.q_xor;
+    qf[s] = __builtin_bit_cast(vec, qw[s]);
+  }
+  f32x16 sacc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      sacc[t] = M::run(__builtin_bit_cast(vec, kw[t][s]), qf[s], s == 0 ? f32x16{} : sacc[t]);
 
   // ---- mask (keys past Nk; causal: keys after the row), exact maximum of
   // the tile, P and its row sum
@@ -199,49 +206,63 @@ __global__ __launch_bounds__(1024) void fa_fwd_short_kernel(Params p) {
         }
   }
 
-  // ---- combine the waves: M = max m_w, L = sum 2^(m_w - M) l_w
+  // ---- combine the waves. Each wave leaves its reference m_w, row sum l_w
+  // and unnormalised O_w (rows = queries) in its own LDS region, which only
+  // it has read so far; after one barrier every thread merges, for its rows
+  // and columns, M = max m_w, L = sum 2^(m_w - M) l_w and
+  // O = sum 2^(m_w - M) O_w / L.
   if (half == 0) {
-    s_m[wave][r32] = m;
+    s_m[wave][r32] = m;  // -inf for a tile with no visible key
     s_l[wave][r32] = l;
   }
-  __syncthreads();  // also: every wave is done with its V tile
-  float Mx = -__builtin_inff();
-  for (int w = 0; w < nw; ++w) Mx = vmax(Mx, s_m[w][r32]);
-  float L = 0.f;
-  for (int w = 0; w < nw; ++w) {
-    const float mw = s_m[w][r32];
-    L += mw == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mw - Mx) * s_l[w][r32];
-  }
-  const float alpha = empty ? 0.f : __builtin_amdgcn_exp2f(m - Mx);
-  // this wave's scaled partial O, rows = queries, in its own LDS region
+  // accumulator registers 4g..4g+3 hold columns 32dt + 8g + 4half .. +3 of
+  // the lane's query: one 16-byte store each
   float* part = (float*)vreg;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      part[r32 * PS + 32 * dt + 8 * (i >> 2) + 4 * half + (i & 3)] = oacc[dt][i] * alpha;
-  if (wave == 0 && half == 0) {
-    s_M[r32] = Mx;
-    s_L[r32] = L;
-  }
+    for (int g = 0; g < 4; ++g)
+      *(f32x4*)(part + r32 * PS + 32 * dt + 8 * g + 4 * half) =
+          f32x4{oacc[dt][4 * g], oacc[dt][4 * g + 1], oacc[dt][4 * g + 2], oacc[dt][4 * g + 3]};
   __syncthreads();
 
-  // ---- sum the partials (two adjacent d per thread), normalise, store
+  // Thread e merges row e / (D/8), columns 8*(e % (D/8)) .. +7.
   T* Oh = head_base<T>(p.o, p.so, hb, hh);
-  for (int e = tid; e < 16 * D; e += 64 * nw) {
-    const int r = (2 * e) / D, d = (2 * e) % D;
+  for (int e = tid; e < 4 * D; e += 64 * nw) {
+    const int r = e / (D / 8), d = 8 * (e % (D / 8));
     if (q0 + r >= Nq) continue;
-    float a0 = 0.f, a1 = 0.f;
-    for (int w = 0; w < nw; ++w) {
-      const float* pw = (const float*)(smem + w * REGION) + r * PS + d;
-      a0 += pw[0];
-      a1 += pw[1];
+    float mw[MAXW];
+    float Mx = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < MAXW; ++w) {
+      mw[w] = w < nw ? s_m[w][r] : -__builtin_inff();
+      Mx = vmax(Mx, mw[w]);
     }
-    const float inv = 1.0f / s_L[r];
-    *(pair*)(Oh + (int64_t)(q0 + r) * p.so.n + d) = M::cvt(a0 * inv, a1 * inv);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < MAXW; ++w) {
+      if (w < nw) {
+        const float f = mw[w] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mw[w] - Mx);
+        const float* pw = (const float*)(smem + w * REGION) + r * PS + d;
+        const f32x4 x0 = *(const f32x4*)pw, x1 = *(const f32x4*)(pw + 4);
+        L += f * s_l[w][r];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[i] += f * x0[i];
+          acc[4 + i] += f * x1[i];
+        }
+      }
+    }
+    const float inv = 1.0f / L;
+    u32x4 ow;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ow[i] = __builtin_bit_cast(uint32_t, M::cvt(acc[2 * i] * inv, acc[2 * i + 1] * inv));
+    *(u32x4*)(Oh + (int64_t)(q0 + r) * p.so.n + d) = ow;
+    if (p.lse != nullptr && d == 0)
+      p.lse[(size_t)head * Nq + q0 + r] = 0.69314718055994531f * (Mx + log2f(L));
   }
-  if (p.lse != nullptr && tid < 32 && q0 + tid < Nq)
-    p.lse[(size_t)head * Nq + q0 + tid] = 0.69314718055994531f * (s_M[tid] + log2f(s_L[tid]));
 }
 
 }  // namespace fa
