@@ -50,6 +50,11 @@
 //     precision; the result is unchanged in exact arithmetic because O and the
 //     row sum carry the same reference. The common path thus needs no row
 //     maximum at all: per score it is one FMA, one exp2 and half a conversion.
+//   * For d <= 64 the block first runs optimistically: the reference comes
+//     from its first tile and is never tested again, so no unit waits for its
+//     row sums. A P too large for its type then shows as a non-finite row
+//     sum or output at the end, and the workgroup redoes the block with the
+//     tests (scores that rise far along the keys; rare for real data).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -129,10 +134,20 @@ __device__ __forceinline__ void work_item(const Params& p, int bid, int& head, i
 // and LSE are written. Otherwise a piece of it: the unnormalised O^T
 // ([D][BM] fp32), the reference maximum and the row sum (each [BM] fp32)
 // go to part, to be merged with the block's other pieces.
+//
+// strict = false is the optimistic pass: the reference maximum is set from
+// the block's first tile (first unit, when pipelined) and never raised after,
+// so no later unit waits for its row sums before P V. A P more than 2^16 above the reference overflows
+// fp16 (or, far beyond, the fp32 row sum) and shows as a non-finite row sum at
+// the end; then nothing is stored and false is returned (the same for every
+// wave of the workgroup), and the caller runs the block again with strict.
+// strict = true raises the reference whenever a unit's row sum leaves
+// (0, 2^15], so P never overflows. (A runtime flag, not a template
+// parameter: one copy of the loop serves both passes.)
 template <int D, int BN, int NW, int RB, int S, bool PIPE, bool CAUSAL, typename T>
-__device__ __forceinline__ void fa_fwd_block(const Params& p, int head, int qb, int t_lo, int t_hi,
+__device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, int t_lo, int t_hi,
                                              float* part, char (&smem)[S][2][BN * D * 2],
-                                             char (&vts)[2][BN * D * 2]) {
+                                             char (&vts)[2][BN * D * 2], bool strict = true) {
   using M = Mma<T>;
   using vec = typename M::vec;
   using pair = typename M::pair;
@@ -158,7 +173,11 @@ __device__ __forceinline__ void fa_fwd_block(const Params& p, int head, int qb, 
   static_assert(S >= 3 && PENDING < 64, "stage count out of range");
 
 
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;
+  // Opaque to the optimiser, so the address arithmetic below is redone in
+  // each pass instead of being hoisted out of the caller's pass loop and
+  // held in registers through both.
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   // Wave index in a scalar register: every per-wave condition below (which
   // row blocks see a tile) must compile to a scalar branch, never to an
@@ -487,7 +506,7 @@ __device__ __forceinline__ void fa_fwd_block(const Params& p, int head, int qb, 
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) psum[t][rb] = exp_unit(sacc[t][rb], -m_run[rb], pf[t][rb]);
-    if (__any(!(unit_ok(psum[0]) && unit_ok(psum[1])))) {
+    if ((strict || j == t_lo) && __any(!(unit_ok(psum[0]) && unit_ok(psum[1])))) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         raise_max(rb, vmax(unit_max(sacc[0][rb]), unit_max(sacc[1][rb])));
@@ -552,7 +571,7 @@ __device__ __forceinline__ void fa_fwd_block(const Params& p, int head, int qb, 
     }
     vec vf[2][NDT];
     load_v(j, t, vf);
-    if (__any(!unit_ok(ps))) {
+    if ((strict || (j == t_lo && t == 0)) && __any(!unit_ok(ps))) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         raise_max(rb, unit_max(sr[rb]));
@@ -629,6 +648,37 @@ __device__ __forceinline__ void fa_fwd_block(const Params& p, int head, int qb, 
     tile_end();
   }
 
+  if (!strict) {
+    // Every row sum finite, or the workgroup redoes the block. The ring is
+    // drained first: the loads past the last tile (zeros) may still be in
+    // flight, and a second pass refills the same stages. Each wave leaves its
+    // verdict in a word of the drained ring.
+    bool bad = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float l_tot = M::kMfmaRowSum ? l_run[rb] : sum_with_partner(l_run[rb]);
+      float om = 0.f;  // bf16 P reaches 2^127 before the row sum overflows: check O too
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) om = vmax(om, __builtin_fabsf(oacc[rb][dt][i]));
+      bad |= !(l_tot < __builtin_inff()) || !(om < __builtin_inff());
+    }
+    const int wave_bad = __any(bad) ? 1 : 0;
+    wait_vmcnt<0>();
+    __syncthreads();
+    int* verdict = (int*)&smem[0][0][0];
+    if (lane == 0) verdict[wave] = wave_bad;
+    __syncthreads();
+    int any_bad = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any_bad |= verdict[w];
+    if (any_bad) {
+      __syncthreads();  // every wave has read the verdicts before the ring refills
+      return false;
+    }
+  }
+
   if (part != nullptr) {
     // ---- a piece of the key range: unnormalised O^T, reference, row sum
 #pragma unroll
@@ -645,7 +695,7 @@ __device__ __forceinline__ void fa_fwd_block(const Params& p, int head, int qb, 
         part[D * BM + BM + row] = l_tot;
       }
     }
-    return;
+    return true;
   }
 
   // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
@@ -671,6 +721,7 @@ __device__ __forceinline__ void fa_fwd_block(const Params& p, int head, int qb, 
         p.lse[(size_t)head * Nq + q_row] = 0.69314718055994531f * (m_run[rb] + log2f(l_tot));
     }
   }
+  return true;
 }
 
 // Waves per SIMD the register allocation must allow. At d = 64 two
@@ -689,7 +740,18 @@ __global__ __launch_bounds__(NW * 64, fwd_min_waves(D)) void fa_fwd_kernel(Param
   __shared__ __attribute__((aligned(1024))) char vts[2][BN * D * 2];
   int head, qb;
   work_item<CAUSAL>(p, blockIdx.x, head, qb);
-  fa_fwd_block<D, BN, NW, RB, S, PIPE, CAUSAL, T>(p, head, qb, 0, 0x7fffffff, nullptr, smem, vts);
+  if constexpr (D <= 64) {
+    // the optimistic pass, then (rarely) the strict one
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass)
+      if (fa_fwd_block<D, BN, NW, RB, S, PIPE, CAUSAL, T>(p, head, qb, 0, 0x7fffffff, nullptr, smem,
+                                                          vts, pass == 1))
+        break;
+  } else {
+    // d = 128: the strict pass alone measured faster (the optimistic form
+    // takes a few registers more and saves no wait at this MFMA share)
+    fa_fwd_block<D, BN, NW, RB, S, PIPE, CAUSAL, T>(p, head, qb, 0, 0x7fffffff, nullptr, smem, vts);
+  }
 }
 
 }  // namespace fa

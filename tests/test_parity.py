@@ -149,6 +149,32 @@ def test_rising_scores():
             compare(o, lse, O, L, what=f"rising scores d={d} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("dtype,jump", [("fp16", 15.5), ("fp16", 17.0), ("bf16", 100.0),
+                                        ("bf16", 140.0)])
+def test_jump_near_overflow(d, dtype, jump):
+    """One key, past the first tile, whose score exceeds everything before it
+    by `jump` (log2 units, i.e. after scale*log2(e)): just below and just
+    above where P relative to a reference taken from the first tile stops
+    fitting fp16 (2^16) or the fp32 output and row sum (bf16, ~2^127). Below,
+    the tiled kernel keeps that reference; above, it must redo the block with
+    a raised one. Both must match the oracle."""
+    require_gpu()
+    note(f"parity jump {jump} d={d} {dtype}")
+    N = 300
+    q, k, v = rand_inputs(1, 2, N, N, d, dtype, seed=4000 + d, v_uniform=True)
+    q = torch.ones_like(q)
+    k = (k.float() * 0.01).to(k.dtype)
+    c = default_scale(d) * 1.4426950408889634
+    k = k.float()
+    k[:, :, 150, :] = jump / (c * d)  # score of key 150 (log2 units): jump
+    k = k.to(q.dtype)
+    for causal in (False, True):
+        O, L = oracle.attention(q, k, v, scale=default_scale(d), causal=causal)
+        o, lse = run_gpu(q, k, v, causal, path="tiled")
+        compare(o, lse, O, L, what=f"jump {jump} d={d} {dtype} causal={causal}")
+
+
 SAMPLE_ROWS = 48
 
 
