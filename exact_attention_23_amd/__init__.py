@@ -130,6 +130,15 @@ def _current_stream(device_index: int):
     return h or None
 
 
+def _current_device() -> int:
+    """Index of the current device (torch's raw getter; the public
+    torch.cuda.current_device adds a lazy-initialisation check per call)."""
+    import torch
+
+    raw = getattr(torch._C, "_cuda_getDevice", None)
+    return raw() if raw is not None else torch.cuda.current_device()
+
+
 def _dtype_code(t) -> int:
     import torch
 
@@ -165,18 +174,23 @@ def attention(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
     """
     import torch
 
+    # Device indices (get_device) rather than torch.device objects, and one
+    # pass over the inputs: at N = 400 the host cost of this wrapper is
+    # comparable to the kernel's.
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
         if t.dim() != 4:
             raise ValueError(f"{name} must be a [B, H, N, d] tensor")
-    if not (q.device == k.device == v.device):
+    dev = q.get_device()
+    if k.get_device() != dev or v.get_device() != dev:
         raise ValueError("q, k, v must be on one device")
-    if not (q.dtype == k.dtype == v.dtype):
+    dt = q.dtype
+    if k.dtype != dt or v.dtype != dt:
         raise ValueError("q, k, v must share a dtype")
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
-    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
+    if k.shape != (B, H, Nk, d) or v.shape != (B, H, Nk, d):
         raise ValueError("k and v must be [B, H, Nk, d] matching q")
     code = _dtype_code(q)
     if path not in _PATHS:
@@ -185,45 +199,44 @@ def attention(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)  # q's strides when q is dense, else contiguous
-    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device:
+    elif out.shape != q.shape or out.dtype != dt or out.get_device() != dev:
         raise ValueError("out must be a tensor like q")
     if lse is None and return_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    elif lse is not None and (tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32
-                              or lse.device != q.device or not lse.is_contiguous()):
+    elif lse is not None and (lse.shape != (B, H, Nq) or lse.dtype != torch.float32
+                              or lse.get_device() != dev or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
     lib = _lib.load()
     contiguous = q.is_contiguous() and k.is_contiguous() and v.is_contiguous() and out.is_contiguous()
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
             lse.data_ptr() if lse is not None else None, B, H, Nq, Nk, d)
-    tail = (float(scale), 1 if causal else 0, code)
+    c = 1 if causal else 0
     use_stream = contiguous and (path == "stream" or (
-        path == "auto" and _stream_advised(lib, q.device.index, B, H, Nq, Nk, d, code,
-                                           1 if causal else 0)))
+        path == "auto" and _stream_advised(lib, dev, B, H, Nq, Nk, d, code, c)))
     if use_stream:
-        st_handle = _current_stream(q.device.index)
+        st_handle = _current_stream(dev)
         nbytes = lib.fa_fwd_stream_workspace_bytes(B, H, Nq, Nk, d, code)
         if nbytes < 0:
             raise FaError(_lib.FA_ERR_LAUNCH, "stream form unavailable on this device")
         ws = _stream_workspace(q.device, st_handle, nbytes)
-        fn, call = lib.fa_fwd_stream, ptrs + tail[:1] + (tail[1], code, ws.data_ptr(), ws.numel())
+        fn, call = lib.fa_fwd_stream, ptrs + (float(scale), c, code, ws.data_ptr(), ws.numel())
     elif contiguous:
-        fn, call = lib.fa_fwd_ex, ptrs + tail + (_PATHS[path],)
+        fn, call = lib.fa_fwd_ex, ptrs + (float(scale), c, code, _PATHS[path])
     else:
         if path != "auto":
             raise ValueError("path applies to contiguous tensors only")
         strides = (_layout_strides(q, "q") + _layout_strides(k, "k") + _layout_strides(v, "v")
                    + _layout_strides(out, "out"))
         arr = (ctypes.c_int64 * 12)(*strides)
-        fn, call = lib.fa_fwd_strided, ptrs + (ctypes.cast(arr, ctypes.c_void_p),) + tail
+        fn, call = lib.fa_fwd_strided, ptrs + (ctypes.cast(arr, ctypes.c_void_p), float(scale), c,
+                                               code)
     # The launch goes to the current device; switch only when q lives elsewhere
     # (the device guard costs several microseconds per call).
-    idx = q.device.index
-    if idx == torch.cuda.current_device():
-        st = fn(*call, _current_stream(idx))
+    if dev == _current_device():
+        st = fn(*call, _current_stream(dev))
     else:
-        with torch.cuda.device(q.device):
-            st = fn(*call, _current_stream(idx))
+        with torch.cuda.device(dev):
+            st = fn(*call, _current_stream(dev))
     _check(st)
     return out, lse
 
