@@ -1,6 +1,6 @@
 // fa_bwd_kernel.hpp - the exact-attention backward kernels for gfx950 (CDNA4).
 //
-// What is computed (the chain rule of the forward definition; the pages say
+// What is computed (the chain rule of the forward definition; the cited articles say
 // training keeps the softmax statistics for the backward pass, kwkr.cn YOLO11
 // FlashAttention-2 article, section 2.3, and that the backward recomputes the
 // weights instead of storing them, "YOLOv12推理速度翻倍秘诀：Flash Attention加持",

@@ -1,6 +1,6 @@
 // fa_fwd_fp8.hpp - the exact-attention forward on FP8 (e4m3) Q, K, V for gfx950.
 //
-// The pages name FP8 as one of FlashAttention-3's additions (ai2ai.xin
+// The cited articles name FP8 as one of FlashAttention-3's additions (ai2ai.xin
 // flash-attention-principle page, FA-3 section). Q, K and V arrive as e4m3
 // bytes with one fp32 dequantisation factor per tensor; the products run on
 // v_mfma_scale_f32_32x32x64_f8f6f4 (64-deep contraction, twice the fp16

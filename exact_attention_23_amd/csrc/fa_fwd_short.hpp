@@ -7,8 +7,8 @@
 // combination of softmaxes over disjoint key ranges: with per-range maxima
 // m_w, sums l_w and unnormalised outputs O_w, the row's maximum is
 // M = max_w m_w, its sum L = sum_w 2^(m_w - M) l_w and its output
-// O = sum_w 2^(m_w - M) O_w / L (exp2 domain). The pages' online update is the
-// sequential form of this combination; here it runs in parallel.
+// O = sum_w 2^(m_w - M) O_w / L (exp2 domain). The articles' online update is
+// the sequential form of this combination; here it runs in parallel.
 //
 // gfx950 mapping
 //   * A workgroup owns 32 query rows of one (batch, head) and one wave per
@@ -21,9 +21,12 @@
 //     ds_read_b64_tr_b16 (two transpose reads give the 8 keys of a fragment).
 //   * Each wave takes the exact maximum of its tile, forms P = 2^(S*c - m_w)
 //     (at most 1), its row sum (fp16: on the matrix cores from the rounded P;
-//     bf16: in fp32) and O_w. The waves then exchange m_w and l_w through LDS,
-//     scale their O_w by 2^(m_w - M) into their LDS regions, and all threads
-//     sum the partials, normalise and store O and LSE.
+//     bf16: in fp32) and O_w, and leaves m_w, l_w and the unnormalised O_w in
+//     LDS (O_w in its own region, which only it has read). After one barrier
+//     each thread merges 8 columns of one row over the waves, normalises and
+//     stores them (and the row's LSE).
+//   * The chain is latency-bound (one tile deep): every Q and K load is
+//     issued before the first MFMA, so it pays one memory round trip.
 #pragma once
 
 #include "fa_fwd_kernel.hpp"

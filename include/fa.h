@@ -10,7 +10,7 @@
  *
  * This is the attention formula of "FlashAttention 深度解读" (coreui.cn), section
  * 背景, and the three-step definition in the kwkr.cn YOLO11 FlashAttention-2
- * article, section 1.1. The library computes it the way those pages (section 原理
+ * article, section 1.1. The library computes it the way those articles (section 原理
  * of the former, section 1.2 of the latter) describe: K and V are streamed in
  * tiles through on-chip memory and each tile updates a running row maximum,
  * a running exponential sum and a rescaled output accumulator, so the score
@@ -226,7 +226,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
  *     dQ  = scale * dS K
  *     dK  = scale * dS^T Q
  *
- * The pages state that training keeps the forward's softmax statistics for
+ * The cited articles state that training keeps the forward's softmax statistics for
  * the backward pass (kwkr.cn YOLO11 FlashAttention-2 article, section 2.3) and
  * that the backward recomputes the attention weights rather than storing them
  * ("YOLOv12推理速度翻倍秘诀：Flash Attention加持", section 1); the formulas are the

@@ -4,12 +4,12 @@ on the CPU.
 TEST INFRASTRUCTURE ONLY (see the package docstring): no product code may
 import this module.
 
-What is computed, and where the pages state it:
+What is computed, and where the cited articles state it:
   * Training runs a backward pass through the attention, for which the
     forward keeps its softmax statistics (kwkr.cn YOLO11 FlashAttention-2
     article, section 2.3), and that backward recomputes the softmax instead of
     storing it ("YOLOv12推理速度翻倍秘诀：Flash Attention加持", section 1, on
-    numerically stable recomputation). The pages give no formulas for it; the
+    numerically stable recomputation). The articles give no formulas for it; the
     plainest reading is the gradient of the forward definition (see
     definition.py) with respect to Q, K and V, for a given upstream gradient
     dO of the output, i.e. the vector-Jacobian product of

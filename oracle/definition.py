@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring): no product code may
 import this module.
 
-What is computed, and where the pages state it:
+What is computed, and where the cited articles state it:
   * O = softmax(Q K^T * scale) V, the three steps being the Q-K product, a row
     softmax, and the product with V ("FlashAttention 深度解读", section 背景,
     its attention formula; kwkr.cn YOLO11 FlashAttention-2 article, section

@@ -4,7 +4,7 @@ This module draws the random Q, K, V tensors that both the HIP path and the
 oracle consume. It holds no attention arithmetic: only shapes, seeds and value
 distributions.
 
-The five named workloads are the attention calls the source pages talk about:
+The five named workloads are the attention calls the cited articles describe:
   * a YOLO C2PSA/PSA attention over a flattened 20x20 feature map
     (YOLO11 FlashAttention-2 replacement article, kwkr.cn, sections 1.1 and 2.2;
     the map is flattened to a 400-long sequence),
