@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -46,11 +47,24 @@ BWD_KERNELS = (("pre", "fa_bwd_pre_kernel", 1), ("dkdv", "fa_bwd_dkdv_kernel", 2
                ("dq", "fa_bwd_dq_kernel", 4))
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines, so that an edit of the
+    comments alone does not mark the profiled kernel as changed."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    out = []
+    for line in text.splitlines():
+        line = re.sub(r"//.*$", "", line).rstrip()
+        if line.strip():
+            out.append(line)
+    return "\n".join(out)
+
+
 def kernel_source_hash(sources=None) -> str:
+    """Hash of the code (comments stripped) of a kernel's source files."""
     h = hashlib.sha256()
     for p in (sources or KERNEL_SOURCES):
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
