@@ -142,10 +142,10 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p) {
 #endif
 
 // Waves per SIMD the backward kernels are compiled for (register budget).
-// d = 64 dK/dV: 198 registers would allow two waves, LDS (42 KB) three; capped
-// at 168 it spills 11 and runs 2-3% faster. d = 32 dQ: 130 registers would
-// allow three waves, capped at 128 (3 spilled) four, 2% faster.
-constexpr int bwd_dkdv_min_waves(int d) { return d == 64 ? 3 : 1; }
+// d = 32 dQ: 130 registers would allow three waves, capped at 128 (3 spilled)
+// four, 2% faster. (d = 64 dK/dV capped at three waves ran 2-3% faster but
+// its 11 spilled registers added 40% to its HBM traffic; it is not capped.)
+constexpr int bwd_dkdv_min_waves(int) { return 1; }
 constexpr int bwd_dq_min_waves(int d) { return d == 32 ? 4 : 1; }
 
 template <int D, int NW, int S, bool CAUSAL, typename T>
