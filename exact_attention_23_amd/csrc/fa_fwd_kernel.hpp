@@ -137,13 +137,14 @@ __device__ __forceinline__ void work_item(const Params& p, int bid, int& head, i
 //
 // strict = false is the optimistic pass: the reference maximum is set from
 // the block's first tile (first unit, when pipelined) and never raised after,
-// so no later unit waits for its row sums before P V. A P more than 2^16 above the reference overflows
-// fp16 (or, far beyond, the fp32 row sum) and shows as a non-finite row sum at
-// the end; then nothing is stored and false is returned (the same for every
-// wave of the workgroup), and the caller runs the block again with strict.
-// strict = true raises the reference whenever a unit's row sum leaves
-// (0, 2^15], so P never overflows. (A runtime flag, not a template
-// parameter: one copy of the loop serves both passes.)
+// so no later unit waits for its row sums before P V. A P more than 2^16
+// above the reference overflows fp16 (bf16: far beyond, the fp32 row sum or
+// output) and shows as a non-finite row sum or output at the end; then
+// nothing is stored and false is returned (the same for every wave of the
+// workgroup), and the caller runs the block again with strict = true, which
+// raises the reference whenever a unit's row sum exceeds 2^15 or is not
+// finite, so P never overflows. (A runtime flag, not a template parameter:
+// one copy of the loop serves both passes.)
 template <int D, int BN, int NW, int RB, int S, bool PIPE, bool CAUSAL, typename T>
 __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, int t_lo, int t_hi,
                                              float* part, char (&smem)[S][2][BN * D * 2],
