@@ -86,7 +86,11 @@ __device__ __forceinline__ int lds_off(int r, int c) {
 // not guard every LDS read with a wait for all such loads in flight; the
 // kernel waits for them itself (wait_vmcnt) before the barrier that publishes
 // a stage. M0 is set inside the same asm block; the load has no register
-// result.
+// result. M0 is a reserved register the compiler does not save around the
+// block (hipcc warns about the clobber); that is safe here because nothing
+// else in these kernels reads M0: in their gfx950 assembly every M0 write is
+// one of these blocks' own, and no instruction that uses M0 (indirect
+// register indexing, LDS-direct or GWS operations, messages) appears.
 __device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr,
                                            uint32_t voffset) {
   asm volatile(
