@@ -174,6 +174,83 @@ def time_fp8(w, steps: int, warmup: int, settle_ms: float = 300.0):
     return ev0.elapsed_time(ev1) / steps
 
 
+def launch_floor_us(calls: int = 100, replays: int = 20) -> float:
+    """Device time per call of a trivial kernel (one-element add) from a
+    replayed HIP graph of `calls` launches: the launch floor that the short
+    sequences' device times sit on."""
+    import torch
+
+    x = torch.zeros(1, device="cuda:0")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        x.add_(1.0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            x.add_(1.0)
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(replays):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) * 1e3 / (replays * calls)
+
+
+def clock_under_load(w, seconds_cap: float = 15.0):
+    """The engine clocks (MHz, mean/min/max over the XCDs) that `amd-smi
+    metric --clock` reports while w's forward runs back to back, or None when
+    the tool is unavailable. The reading is a snapshot taken once the load has
+    run for a moment."""
+    import shutil
+    import subprocess
+    import threading
+
+    import torch
+
+    import exact_attention_23_amd as fa
+
+    tool = shutil.which("amd-smi")
+    if tool is None:
+        return None
+    result = {}
+
+    def sample():
+        time.sleep(0.5)
+        try:
+            r = subprocess.run([tool, "metric", "--clock", "--json"], capture_output=True, text=True,
+                               timeout=seconds_cap)
+            data = json.loads(r.stdout)
+            gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
+            clk = [v["clk"]["value"] for k, v in gpu["clock"].items() if k.startswith("gfx_")]
+            result["mhz"] = [float(x) for x in clk if isinstance(x, (int, float))]
+        except Exception as e:  # noqa: BLE001 - report the clock as unknown
+            result["error"] = str(e)
+
+    dev = torch.device("cuda:0")
+    q, k, v, o = layout_inputs(w, "bhnd", dev)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    th = threading.Thread(target=sample, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    while th.is_alive() and time.perf_counter() - t0 < seconds_cap:
+        for _ in range(8):
+            fa.attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        torch.cuda.synchronize()
+    th.join(timeout=1.0)
+    mhz = result.get("mhz")
+    if not mhz:
+        return None
+    return {"mean": round(sum(mhz) / len(mhz), 1), "min": min(mhz), "max": max(mhz),
+            "xcds": len(mhz), "tool": "amd-smi metric --clock (snapshot under load)"}
+
+
 def time_graph(w, calls: int = 100, replays: int = 20):
     """Device time per call (µs) with the host's launch cost taken out: `calls`
     back-to-back calls captured in one HIP graph, replayed `replays` times
@@ -501,6 +578,8 @@ def main(argv=None):
                     help="fwd (default): the forward line, with the backward of the same "
                          "workload attached; bwd: a line for the backward pass alone")
     ap.add_argument("--no-bwd", action="store_true", help="leave the backward out of the fwd line")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="do not sample the engine clock (amd-smi) under the workload's load")
     ap.add_argument("--fp8", action="store_true",
                     help="forward on the workload's inputs quantised to e4m3 (fa_fwd_fp8), "
                          "against the fp8 matrix peak")
@@ -574,9 +653,12 @@ def main(argv=None):
         n400_eager_us = time_gpu(WORKLOADS["yolo20"], max(args.steps, 50), args.warmup,
                                  args.settle_ms) * 1e3
     short = None
+    floor_us = None
     if not args.no_n400 and args.workload != "yolo20":
         # the two latency-bound sizes (20x20 and 19x19 maps): HBM rate and latency spread
         short = {n: short_stats(WORKLOADS[n]) for n in ("yolo20", "tail361")}
+        floor_us = launch_floor_us()
+    clock = None if args.no_clock or args.layout != "bhnd" else clock_under_load(w)
     traffic = measured_traffic(w.name)
     line = {
         "metric": METRIC,
@@ -602,6 +684,8 @@ def main(argv=None):
         "us_per_call_n400": None if n400_us is None else round(n400_us, 3),
         "us_per_call_n400_eager": None if n400_eager_us is None else round(n400_eager_us, 3),
         "short_sequences": short,
+        "launch_floor_us": None if floor_us is None else round(floor_us, 3),
+        "clock_mhz_under_load": clock,
         "mfma_peak_frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
