@@ -597,7 +597,7 @@ def main(argv=None):
         copy_calibration(args.copy_calibration_mib)
         return 0
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported. "
+        print(f"bench.py: the benchmark runs on one GPU only; --gpus {args.gpus} is not supported. "
               "The path shards over (batch, head) with no exchange, so per-GPU work is the "
               "single-GPU kernel at a fraction of the heads.", file=sys.stderr)
         return 2
