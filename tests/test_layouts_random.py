@@ -1,0 +1,78 @@
+"""The strided forward (fa_fwd_strided) on seeded random shapes and layouts.
+
+Each case draws batch, heads, both sequence lengths (1 to 700), head width,
+type and mask, and for each of q, k, v and the output one layout:
+contiguous, sequence-major [B, N, H, d] (viewed as [B, H, N, d]), or rows
+padded by 8 or 24 elements. Results are compared element by element with the
+fp64 oracle on the contiguous originals, and the padding around a padded
+output must keep its sentinel. The draws are fixed by the seed, so a failure
+names a reproducible case.
+
+fp16 cases are held to the stated bar (max|dO| <= 1e-2, mean <= 1e-3,
+|dLSE| <= 1e-3). bf16 cases are held to the bound derived from the arithmetic
+(compare_derived) and the stated mean bar: an early causal row sees only a
+few keys, so |O| reaches ~2, where half an ulp of the bf16 output alone is
+0.0078 and the rounded P adds the rest of a 1e-2 excess."""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_23_amd as fa
+import oracle
+from tests.gpu_util import compare, compare_derived, default_scale, note, rand_inputs, require_gpu
+from tests.test_layouts import bnhd_view, padded_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+N_CASES = 16
+IN_LAYOUTS = ["contig", "seqmajor", "pad8", "pad24"]
+OUT_LAYOUTS = ["contig", "seqmajor", "pad8"]
+
+
+def _cases():
+    rng = np.random.default_rng(20240923)
+    out = []
+    for i in range(N_CASES):
+        out.append(dict(
+            B=int(rng.integers(1, 4)), H=int(rng.integers(1, 5)),
+            Nq=int(rng.integers(1, 701)), Nk=int(rng.integers(1, 701)),
+            d=int(rng.choice([32, 64, 128])), dtype=str(rng.choice(["fp16", "bf16"])),
+            causal=bool(rng.integers(0, 2)),
+            lay=tuple(str(rng.choice(IN_LAYOUTS)) for _ in range(3)) + (str(rng.choice(OUT_LAYOUTS)),),
+            seed=9000 + i))
+    return out
+
+
+def _place(t, kind):
+    """t ([B, H, N, d], host) on the GPU in layout `kind`, as a [B, H, N, d] view; also the
+    padded buffer when there is one."""
+    if kind == "contig":
+        return t.to(DEV), None
+    if kind == "seqmajor":
+        return bnhd_view(t), None
+    return padded_rows(t, int(kind[3:]))
+
+
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: "B{B}H{H}_q{Nq}k{Nk}_d{d}_{dtype}_{m}_{l}".format(
+    m="causal" if c["causal"] else "full", l="-".join(c["lay"]), **c))
+def test_random_layout(case):
+    require_gpu()
+    c = case
+    note(f"layout random {c}")
+    q, k, v = rand_inputs(c["B"], c["H"], c["Nq"], c["Nk"], c["d"], c["dtype"], seed=c["seed"])
+    (qv, _), (kv, _), (vv, _) = (_place(t, kind) for t, kind in zip((q, k, v), c["lay"][:3]))
+    ov, obuf = _place(torch.zeros_like(q), c["lay"][3])
+    o, lse = fa.attention(qv, kv, vv, causal=c["causal"], out=ov)
+    torch.cuda.synchronize()
+    if obuf is not None:
+        assert bool((obuf[..., c["d"]:] == -7.0).all()), f"{c}: padding of the output was written"
+    scale = default_scale(c["d"])
+    if c["dtype"] == "bf16":
+        compare_derived(o.cpu(), lse.cpu(), q, k, v, scale, c["causal"], what=str(c))
+        O, _ = oracle.attention(q, k, v, scale=scale, causal=c["causal"])
+        mean = float(np.abs(o.cpu().double().numpy() - O).mean())
+        assert mean <= 1e-3, f"{c}: mean|dO|={mean:.3e}"
+        return
+    O, L = oracle.attention(q, k, v, scale=scale, causal=c["causal"])
+    compare(o.cpu(), lse.cpu(), O, L, what=str(c))

@@ -3,11 +3,12 @@
 kernel drawn at random, each compared element by element with the oracle.
 The draws are fixed by the seed, so a failure names a reproducible case.
 
-The bar is the stated one (max|dO| <= 1e-2, mean <= 1e-3, |dLSE| <= 1e-3),
-except for bf16 with a scale beyond 1/sqrt(d): logits of several units make
-rows nearly one-hot with |O| up to ~4, where half an ulp of bf16 output alone
-reaches 0.0078-0.0156; those cases are held to the bound derived from the
-arithmetic (compare_derived)."""
+fp16 cases are held to the stated bar (max|dO| <= 1e-2, mean <= 1e-3,
+|dLSE| <= 1e-3). bf16 cases are held to the bound derived from the arithmetic
+(compare_derived) and the stated mean bar: logits of several units (a scale
+beyond 1/sqrt(d)) make rows nearly one-hot, and the first rows of a causal
+mask see only a few keys; either way |O| reaches 2-4, where half an ulp of
+the bf16 output alone is 0.0078-0.0156."""
 import math
 
 import numpy as np
@@ -47,8 +48,11 @@ def test_random_shape(case):
     q, k, v = rand_inputs(c["B"], c["H"], c["Nq"], c["Nk"], c["d"], c["dtype"], seed=c["seed"])
     o, lse = run_gpu(q, k, v, c["causal"], scale=c["scale"], path=c["path"])
     scale = c["scale"] if c["scale"] is not None else 1.0 / math.sqrt(c["d"])
-    if c["dtype"] == "bf16" and abs(scale) > 1.0 / math.sqrt(c["d"]):
+    if c["dtype"] == "bf16":
         compare_derived(o, lse, q, k, v, scale, c["causal"], what=str(c))
+        O, _ = oracle.attention(q, k, v, scale=scale, causal=c["causal"])
+        mean = float(np.abs(o.double().numpy() - O).mean())
+        assert mean <= 1e-3, f"{c}: mean|dO|={mean:.3e}"
         return
     O, L = oracle.attention(q, k, v, scale=scale, causal=c["causal"])
     compare(o, lse, O, L, what=str(c))
