@@ -7,6 +7,7 @@ missing library or an unsupported argument raises.
 """
 from __future__ import annotations
 
+import collections
 import ctypes
 import math
 from typing import Optional, Tuple
@@ -15,14 +16,17 @@ from . import _lib
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_FP16, FA_OK, FA_PATH_AUTO,  # noqa: F401
                    FA_PATH_SHORT, FA_PATH_TILED)
 
-__all__ = ["FaError", "fa_fwd", "fa_fwd_ex", "fa_fwd_strided", "attention_fp8", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_bytes", "attention",
-           "attention_backward", "flash_attention", "version"]
+__all__ = ["FaError", "fa_fwd", "fa_fwd_ex", "fa_fwd_strided", "attention_fp8", "fa_bwd",
+           "fa_bwd_ex", "fa_bwd_workspace_bytes", "attention", "attention_backward",
+           "flash_attention", "release_workspaces", "version"]
 
 _PATHS = {"auto": FA_PATH_AUTO, "tiled": FA_PATH_TILED, "short": FA_PATH_SHORT, "stream": -1}
 
 # Workspaces of the stream form, one per (device, stream): calls on one stream
-# run in order, so they can share it.
-_STREAM_WS = {}
+# run in order, so they can share it. At most _STREAM_WS_MAX are kept (the
+# least recently used goes first); release_workspaces() drops them all.
+_STREAM_WS = collections.OrderedDict()
+_STREAM_WS_MAX = 4
 
 
 _ADVISED = {}
@@ -41,14 +45,34 @@ def _stream_advised(lib, device_index, *shape) -> bool:
 
 
 def _stream_workspace(device, stream, nbytes):
+    """The stream form's workspace for (device, stream), or None when none
+    large enough exists and the current stream is being captured into a
+    graph (memory allocated there would belong to the graph's private pool
+    and outlive nothing but the graph)."""
     import torch
 
     key = (device.index, stream)
     ws = _STREAM_WS.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        _STREAM_WS[key] = ws
+    if ws is not None and ws.numel() >= nbytes:
+        _STREAM_WS.move_to_end(key)
+        return ws
+    if torch.cuda.is_current_stream_capturing():
+        return None
+    # Freed memory goes back to torch's caching allocator on the stream it was
+    # allocated on, which is the stream that used it, so reuse stays ordered
+    # after the kernels that read it.
+    _STREAM_WS.pop(key, None)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _STREAM_WS[key] = ws
+    while len(_STREAM_WS) > _STREAM_WS_MAX:
+        _STREAM_WS.popitem(last=False)
     return ws
+
+
+def release_workspaces() -> None:
+    """Drop every cached workspace of the stream form (they are re-created,
+    outside graph capture, on the next call that needs one)."""
+    _STREAM_WS.clear()
 
 
 class FaError(RuntimeError):
@@ -219,10 +243,17 @@ def attention(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
         if nbytes < 0:
             raise FaError(_lib.FA_ERR_LAUNCH, "stream form unavailable on this device")
         ws = _stream_workspace(q.device, st_handle, nbytes)
-        fn, call = lib.fa_fwd_stream, ptrs + (float(scale), c, code, ws.data_ptr(), ws.numel())
-    elif contiguous:
+        if ws is None:
+            if path == "stream":
+                raise FaError(_lib.FA_ERR_WORKSPACE,
+                              "the stream form's workspace is not allocated during graph capture: "
+                              "call attention(..., path='stream') once on this stream before capturing")
+            use_stream = False  # the automatic choice takes the tiled kernel instead
+        else:
+            fn, call = lib.fa_fwd_stream, ptrs + (float(scale), c, code, ws.data_ptr(), ws.numel())
+    if not use_stream and contiguous:
         fn, call = lib.fa_fwd_ex, ptrs + (float(scale), c, code, _PATHS[path])
-    else:
+    elif not use_stream:
         if path != "auto":
             raise ValueError("path applies to contiguous tensors only")
         strides = (_layout_strides(q, "q") + _layout_strides(k, "k") + _layout_strides(v, "v")

@@ -273,7 +273,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
     const StreamVariant sv = pick_stream_dt(dtype, d);
     const int64_t G = stream_grid(sv);
     const int64_t nblocks = B * H * ((Nq + sv.bm - 1) / sv.bm);
-    const int64_t need = G * 2 * (int64_t)sv.bm * (d + 2) * 4;
+    const int64_t need = G * 2 * (int64_t)sv.bm * (d + 3) * 4;
     if (G < 1) return fa::launch_status(hipErrorInvalidDeviceFunction);
     if (workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (fa::overlaps(workspace, (size_t)need, q, q_bytes) || fa::overlaps(workspace, (size_t)need, k, k_bytes) ||
@@ -341,7 +341,7 @@ int64_t fa_fwd_stream_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t 
   const StreamVariant sv = pick_stream_dt(dtype, d);
   const int64_t G = stream_grid(sv);
   if (G < 1) return -1;
-  return G * 2 * (int64_t)sv.bm * (d + 2) * 4;
+  return G * 2 * (int64_t)sv.bm * (d + 3) * 4;
 }
 
 int fa_fwd_stream_advised(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype,

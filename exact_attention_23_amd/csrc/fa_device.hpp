@@ -22,6 +22,15 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // Word 3 of a raw buffer resource on gfx9: 32-bit data format, no swizzle.
 constexpr int kBufferFlags = 0x00020000;
 
+// Row sums of P. O is divided by the sum of the P values the P V product
+// actually used (P rounded to the input type), taken on the matrix cores: a
+// 16x16x32 MFMA of a 0/1 selector against the P operand (see the kernels'
+// row_sel). Rounding errors of the individual weights then cancel against the
+// same errors in the normaliser, so a row dominated by one key returns that
+// key's V row to within the output's own rounding. For fp16 the log-sum-exp
+// comes from the same sum (11 bits: ln of it moves by at most 2^-11); bf16
+// keeps 8 bits, so its log-sum-exp takes a second sum of the unrounded fp32
+// values (kLse32), accumulated per lane while P is formed.
 template <typename T> struct Mma;
 template <> struct Mma<_Float16> {
   typedef f16x8 vec;
@@ -34,11 +43,15 @@ template <> struct Mma<_Float16> {
     f32x2 f = {lo, hi};
     return __builtin_convertvector(f, pair);
   }
-  // The row sum is taken on the matrix cores from the same rounded P that
-  // enters P V (see row_sum_mfma); fp16 keeps 11 bits, so the sum, and ln of
-  // it, move by at most 2^-11 relative.
-  static constexpr bool kMfmaRowSum = true;
-  static __device__ __forceinline__ float row_sum(float, float, pair, float acc) { return acc; }
+  static __device__ __forceinline__ vec selector(bool on) {
+    const _Float16 x = on ? (_Float16)1.0f : (_Float16)0.0f;
+    return vec{x, x, x, x, x, x, x, x};
+  }
+  static __device__ __forceinline__ f32x4 sel_sum(vec sel, vec pr, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(sel, pr, acc, 0, 0, 0);
+  }
+  static constexpr bool kLse32 = false;
+  static __device__ __forceinline__ float lse_sum(float, float, float acc) { return acc; }
 };
 template <> struct Mma<__bf16> {
   typedef bf16x8 vec;
@@ -50,10 +63,15 @@ template <> struct Mma<__bf16> {
     f32x2 f = {lo, hi};
     return __builtin_convertvector(f, pair);
   }
-  // bf16 keeps only 8 bits, so the row sum is taken from the fp32 values to
-  // hold the log-sum-exp to fp32 accuracy.
-  static constexpr bool kMfmaRowSum = false;
-  static __device__ __forceinline__ float row_sum(float p0, float p1, pair, float acc) {
+  static __device__ __forceinline__ vec selector(bool on) {
+    const __bf16 x = on ? (__bf16)1.0f : (__bf16)0.0f;
+    return vec{x, x, x, x, x, x, x, x};
+  }
+  static __device__ __forceinline__ f32x4 sel_sum(vec sel, vec pr, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pr, acc, 0, 0, 0);
+  }
+  static constexpr bool kLse32 = true;
+  static __device__ __forceinline__ float lse_sum(float p0, float p1, float acc) {
     return acc + (p0 + p1);
   }
 };

@@ -36,12 +36,13 @@
 //     tile publishes a stage to the workgroup. LDS rows are XOR-swizzled in
 //     16-byte chunks against bank conflicts.
 //   * exp is v_exp_f32 (2^x) on scores scaled by scale*log2(e), folded into one
-//     FMA with the reference maximum. For fp16 the row sum is taken on the
-//     matrix cores (a 16x16x32 MFMA against a 0/1 selector) from the same
-//     rounded P that enters the P V product, so the normalisation matches the
-//     weights actually applied and the vector units are spared; for bf16 it is
-//     summed in fp32 before rounding, since 8-bit rounding would move the
-//     log-sum-exp by up to 2^-9.
+//     FMA with the reference maximum. The row sum that normalises O is taken
+//     on the matrix cores (a 16x16x32 MFMA against a 0/1 selector) from the
+//     same rounded P that enters the P V product, so the normalisation
+//     matches the weights actually applied and the vector units are spared.
+//     fp16 takes its log-sum-exp from that sum too; bf16 also sums the fp32 P
+//     before rounding for the log-sum-exp, since 8-bit rounding would move it
+//     by up to 2^-9.
 //   * The reference maximum lags the true running maximum: P of a tile is
 //     formed against it first, and only when that tile's row sum exceeds 2^15
 //     (or is not finite, as on a row's first tile) is the maximum of the tile
@@ -132,8 +133,9 @@ __device__ __forceinline__ void work_item(const Params& p, int bid, int& head, i
 // One query block (head, qb) over key tiles [t_lo, t_hi) (clipped to the
 // tiles the block sees). part == nullptr: the block's whole key range, so O
 // and LSE are written. Otherwise a piece of it: the unnormalised O^T
-// ([D][BM] fp32), the reference maximum and the row sum (each [BM] fp32)
-// go to part, to be merged with the block's other pieces.
+// ([D][BM] fp32), the reference maximum, the log-sum-exp's row sum and the
+// normaliser's row sum (each [BM] fp32) go to part, to be merged with the
+// block's other pieces.
 //
 // strict = false is the optimistic pass: the reference maximum is set from
 // the block's first tile (first unit, when pipelined) and never raised after,
@@ -229,24 +231,26 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
     for (int t = 0; t < NDT; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[rb][t][i] = 0.f;
-  // Running reference maximum (exp2 domain) and row sum relative to it. For
-  // fp16 l_run is the whole row's sum; for bf16 it covers the lane's half of
-  // the keys and is combined with the partner lane at the end.
-  float m_run[RB], l_run[RB];
+  // Running reference maximum (exp2 domain) and row sums relative to it:
+  // l_run, the whole row's sum of the rounded P (the normaliser of O, and for
+  // fp16 also the log-sum-exp's), and for bf16 l32_run, the sum of the
+  // unrounded fp32 P over the lane's half of the keys (the log-sum-exp's;
+  // combined with the partner lane at the end).
+  float m_run[RB], l_run[RB], l32_run[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m_run[rb] = -__builtin_inff();
     l_run[rb] = 0.f;
+    l32_run[rb] = 0.f;
   }
-  // A operand of the fp16 row-sum MFMA (16x16x32): lane l holds row l%16 of the
+  // A operand of the row-sum MFMA (16x16x32): lane l holds row l%16 of the
   // 16x32 selector, for k group l/16. Row m picks the k groups of its own
   // query: A[m][k] = 1 iff (m/4)%2 == (k/8)%2. With B = the P operand (lane l
   // supplies k group l/16 of column l%16, i.e. 8 keys of query l%32), output
   // row m of column n sums the 16 keys of query n + 16*((m/4)%2), and the
   // 16x16 output layout puts rows 4*(l/16)..+3 of column l%16 in lane l: the
   // lane's own query l%32.
-  const _Float16 sel_h = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? (_Float16)1.0f : (_Float16)0.0f;
-  const f16x8 row_sel = {sel_h, sel_h, sel_h, sel_h, sel_h, sel_h, sel_h, sel_h};
+  const vec row_sel = M::selector((((lane & 15) >> 2) & 1) == ((lane >> 4) & 1));
   const float c = p.c;
 
   // ---- tile loads (HBM -> LDS). Load i of this wave fills the 1 KB block
@@ -329,16 +333,17 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
 
   // The work is a sequence of units, one per 32-key subtile t of tile j
   // (unit u = 2j + t). Registers per unit: its scores, its P (B operands) and
-  // its row sum, double-buffered by t.
+  // its row sums (rounded; bf16 also fp32), double-buffered by t.
   static_assert(NSUB == 2, "a tile is two 32-key units");
   f32x16 sacc[2][RB];
   vec pf[2][RB][2];
-  float psum[2][RB];
+  float psum[2][RB], ps32[2][RB];
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       psum[b][rb] = 0.f;
+      ps32[b][rb] = 0.f;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) pf[b][rb][s2] = vec{};
     }
@@ -388,25 +393,19 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
     }
   };
 
-  // Row sum of a unit's P: for fp16, two 16x16x32 MFMAs of the selector
-  // against the rounded P (each lane gets its own query's sum); for bf16 the
-  // fp32 partial sum accumulated while P was formed.
-  auto sub_sum = [&](float lsum, const vec (&pr)[2]) -> float {
-    if constexpr (M::kMfmaRowSum) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // Row sum of a unit's rounded P: two 16x16x32 MFMAs of the selector
+  // against the P operands (each lane gets its own query's sum).
+  auto sub_sum = [&](const vec (&pr)[2]) -> float {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(row_sel, __builtin_bit_cast(f16x8, pr[s2]), acc,
-                                                     0, 0, 0);
-      return acc[0];
-    } else {
-      return lsum;
-    }
+    for (int s2 = 0; s2 < 2; ++s2) acc = M::sel_sum(row_sel, pr[s2], acc);
+    return acc[0];
   };
 
   // P = 2^(S*c - m) of one row block's unit, rounded in pairs into its two B
-  // operands; returns its row sum.
-  auto exp_unit = [&](const f32x16& sr, float negm, vec (&pr)[2]) {
+  // operands; returns its row sum of the rounded P, and in l32 (bf16) the
+  // lane's fp32 sum of the unrounded P.
+  auto exp_unit = [&](const f32x16& sr, float negm, vec (&pr)[2], float& l32) {
     float lsum = 0.f;
     u32x4 w[2];
 #pragma unroll
@@ -414,12 +413,13 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[2 * i], c, negm));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[2 * i + 1], c, negm));
       const pair pp = M::cvt(p0, p1);
-      lsum = M::row_sum(p0, p1, pp, lsum);
+      lsum = M::lse_sum(p0, p1, lsum);
       w[i >> 2][i & 3] = __builtin_bit_cast(uint32_t, pp);
     }
     pr[0] = __builtin_bit_cast(vec, w[0]);
     pr[1] = __builtin_bit_cast(vec, w[1]);
-    return sub_sum(lsum, pr);
+    l32 = lsum;
+    return sub_sum(pr);
   };
 
   // Row maximum of a unit's scores, in the exp2 domain (both lanes of the
@@ -443,6 +443,7 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[rb][dt][i] *= alpha;
     l_run[rb] *= alpha;
+    l32_run[rb] *= alpha;
     m_run[rb] = m_new;
   };
   // A unit's row sum bounds every P of the row, so a sum within
@@ -506,17 +507,22 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) psum[t][rb] = exp_unit(sacc[t][rb], -m_run[rb], pf[t][rb]);
+      for (int rb = 0; rb < RB; ++rb)
+        psum[t][rb] = exp_unit(sacc[t][rb], -m_run[rb], pf[t][rb], ps32[t][rb]);
     if ((strict || j == t_lo) && __any(!(unit_ok(psum[0]) && unit_ok(psum[1])))) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         raise_max(rb, vmax(unit_max(sacc[0][rb]), unit_max(sacc[1][rb])));
 #pragma unroll
-        for (int t = 0; t < 2; ++t) psum[t][rb] = exp_unit(sacc[t][rb], -m_run[rb], pf[t][rb]);
+        for (int t = 0; t < 2; ++t)
+          psum[t][rb] = exp_unit(sacc[t][rb], -m_run[rb], pf[t][rb], ps32[t][rb]);
       }
     }
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) l_run[rb] += psum[0][rb] + psum[1][rb];
+    for (int rb = 0; rb < RB; ++rb) {
+      l_run[rb] += psum[0][rb] + psum[1][rb];
+      if constexpr (M::kLse32) l32_run[rb] += ps32[0][rb] + ps32[1][rb];
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       vec vf[2][NDT];
@@ -536,7 +542,7 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
   constexpr int NMF = RB * KS;  // Q K^T MFMAs of a unit
   constexpr int NPR = RB * 8;   // P pairs of a unit
   auto piped_unit = [&](auto mask_tag, int j, int t, f32x16 (&sr)[RB], vec (&pr)[RB][2],
-                        float (&ps)[RB], const vec (&kf)[KS], f32x16 (&sn)[RB]) {
+                        float (&ps)[RB], float (&p32)[RB], const vec (&kf)[KS], f32x16 (&sn)[RB]) {
     if (decltype(mask_tag)::value) mask_unit(j, t, sr);
     float negm[RB], lsum[RB];
     u32x4 w[RB][2];
@@ -557,7 +563,7 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
               const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[rq][2 * i], c, negm[rq]));
               const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[rq][2 * i + 1], c, negm[rq]));
               const pair pq = M::cvt(p0, p1);
-              lsum[rq] = M::row_sum(p0, p1, pq, lsum[rq]);
+              lsum[rq] = M::lse_sum(p0, p1, lsum[rq]);
               w[rq][i >> 2][i & 3] = __builtin_bit_cast(uint32_t, pq);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -568,7 +574,8 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
     for (int rb = 0; rb < RB; ++rb) {
       pr[rb][0] = __builtin_bit_cast(vec, w[rb][0]);
       pr[rb][1] = __builtin_bit_cast(vec, w[rb][1]);
-      ps[rb] = sub_sum(lsum[rb], pr[rb]);
+      ps[rb] = sub_sum(pr[rb]);
+      p32[rb] = lsum[rb];
     }
     vec vf[2][NDT];
     load_v(j, t, vf);
@@ -576,23 +583,26 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         raise_max(rb, unit_max(sr[rb]));
-        ps[rb] = exp_unit(sr[rb], -m_run[rb], pr[rb]);
+        ps[rb] = exp_unit(sr[rb], -m_run[rb], pr[rb], p32[rb]);
       }
     }
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) l_run[rb] += ps[rb];
+    for (int rb = 0; rb < RB; ++rb) {
+      l_run[rb] += ps[rb];
+      if constexpr (M::kLse32) l32_run[rb] += p32[rb];
+    }
     pv(vf, pr);
   };
   auto piped_tile = [&](auto mask_tag, int j) {
     {  // unit (j, 0), with Q K^T of unit (j, 1)
       vec kf[KS];
       load_k(j, 1, kf);
-      piped_unit(mask_tag, j, 0, sacc[0], pf[0], psum[0], kf, sacc[1]);
+      piped_unit(mask_tag, j, 0, sacc[0], pf[0], psum[0], ps32[0], kf, sacc[1]);
     }
     {  // unit (j, 1), with Q K^T of unit (j+1, 0)
       vec kf[KS];
       load_k(j + 1, 0, kf);
-      piped_unit(mask_tag, j, 1, sacc[1], pf[1], psum[1], kf, sacc[0]);
+      piped_unit(mask_tag, j, 1, sacc[1], pf[1], psum[1], ps32[1], kf, sacc[0]);
     }
     tile_end();
   };
@@ -657,7 +667,7 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
     bool bad = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float l_tot = M::kMfmaRowSum ? l_run[rb] : sum_with_partner(l_run[rb]);
+      const float l_tot = l_run[rb] + (M::kLse32 ? l32_run[rb] : 0.f);
       float om = 0.f;  // bf16 P reaches 2^127 before the row sum overflows: check O too
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
@@ -685,7 +695,7 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int row = wave * WR + 32 * rb + r32;  // row within the block
-      const float l_tot = M::kMfmaRowSum ? l_run[rb] : sum_with_partner(l_run[rb]);
+      const float l_lse = M::kLse32 ? sum_with_partner(l32_run[rb]) : l_run[rb];
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -693,7 +703,8 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
           part[(32 * dt + 8 * (i >> 2) + 4 * half + (i & 3)) * BM + row] = oacc[rb][dt][i];
       if (half == 0) {
         part[D * BM + row] = m_run[rb];
-        part[D * BM + BM + row] = l_tot;
+        part[D * BM + BM + row] = l_lse;
+        part[D * BM + 2 * BM + row] = l_run[rb];
       }
     }
     return true;
@@ -703,8 +714,8 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int q_row = wave_q0 + 32 * rb + r32;
-    const float l_tot = M::kMfmaRowSum ? l_run[rb] : sum_with_partner(l_run[rb]);
-    const float inv = 1.0f / l_tot;
+    const float l_lse = M::kLse32 ? sum_with_partner(l32_run[rb]) : l_run[rb];
+    const float inv = 1.0f / l_run[rb];
     if (q_row < Nq) {
       T* Oh = head_base<T>(p.o, p.so, hb, hh) + (int64_t)q_row * p.so.n;
 #pragma unroll
@@ -719,7 +730,7 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
           *(u32x2*)(Oh + 32 * dt + 8 * g + 4 * half) = w;
         }
       if (p.lse != nullptr && half == 0)
-        p.lse[(size_t)head * Nq + q_row] = 0.69314718055994531f * (m_run[rb] + log2f(l_tot));
+        p.lse[(size_t)head * Nq + q_row] = 0.69314718055994531f * (m_run[rb] + log2f(l_lse));
     }
   }
   return true;

@@ -20,9 +20,10 @@
 //     region; the V^T operands of P V come from that region through
 //     ds_read_b64_tr_b16 (two transpose reads give the 8 keys of a fragment).
 //   * Each wave takes the exact maximum of its tile, forms P = 2^(S*c - m_w)
-//     (at most 1), its row sum (fp16: on the matrix cores from the rounded P;
-//     bf16: in fp32) and O_w, and leaves m_w, l_w and the unnormalised O_w in
-//     LDS (O_w in its own region, which only it has read). After one barrier
+//     (at most 1), its row sum on the matrix cores from the rounded P (the
+//     normaliser of O; for bf16 also the fp32 sum of the unrounded P, for the
+//     LSE) and O_w, and leaves m_w, the sums and the unnormalised O_w in LDS
+//     (O_w in its own region, which only it has read). After one barrier
 //     each thread merges 8 columns of one row over the waves, normalises and
 //     stores them (and the row's LSE).
 //   * The chain is latency-bound (one tile deep): every Q and K load is
@@ -51,7 +52,8 @@ __global__ __launch_bounds__(1024) void fa_fwd_short_kernel(Params p) {
   constexpr int REGION = 32 * PS * 4;       // per-wave LDS bytes: partial O ...
   static_assert(REGION >= 64 * D * 2, "... and, before it, the wave's V tile");
   __shared__ __attribute__((aligned(1024))) char smem[MAXW * REGION];
-  __shared__ float s_m[MAXW][32], s_l[MAXW][32];
+  // per wave and row: reference, normaliser sum, log-sum-exp sum
+  __shared__ float s_m[MAXW][32], s_l[MAXW][32], s_l32[MAXW][32];
 
   const int head = blockIdx.x / p.num_qb;
   const int qb = blockIdx.x - head * p.num_qb;
@@ -154,28 +156,24 @@ __global__ __launch_bounds__(1024) void fa_fwd_short_kernel(Params p) {
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][2 * i], c, negm));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][2 * i + 1], c, negm));
       const pair pp = M::cvt(p0, p1);
-      lsum = M::row_sum(p0, p1, pp, lsum);
+      lsum = M::lse_sum(p0, p1, lsum);
       w[i >> 2][i & 3] = __builtin_bit_cast(uint32_t, pp);
     }
     pf[t][0] = __builtin_bit_cast(vec, w[0]);
     pf[t][1] = __builtin_bit_cast(vec, w[1]);
   }
-  float l;
-  if constexpr (M::kMfmaRowSum) {
-    // selector of the tiled kernel: lane l's sum lands in every register
-    const _Float16 sel_h =
-        (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? (_Float16)1.0f : (_Float16)0.0f;
-    const f16x8 row_sel = {sel_h, sel_h, sel_h, sel_h, sel_h, sel_h, sel_h, sel_h};
+  // row sum of the rounded P (selector of the tiled kernel: lane l's sum
+  // lands in every register), and for bf16 the fp32 sum for the LSE
+  float l, l32;
+  {
+    const vec row_sel = M::selector((((lane & 15) >> 2) & 1) == ((lane >> 4) & 1));
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(row_sel, __builtin_bit_cast(f16x8, pf[t][s2]), acc,
-                                                     0, 0, 0);
+      for (int s2 = 0; s2 < 2; ++s2) acc = M::sel_sum(row_sel, pf[t][s2], acc);
     l = acc[0];
-  } else {
-    l = sum_with_partner(lsum);
+    l32 = M::kLse32 ? sum_with_partner(lsum) : l;
   }
 
   // ---- O_w^T = V^T P^T. The V^T fragment for d tile dt, unit t, half s2 is
@@ -209,14 +207,16 @@ __global__ __launch_bounds__(1024) void fa_fwd_short_kernel(Params p) {
         }
   }
 
-  // ---- combine the waves. Each wave leaves its reference m_w, row sum l_w
-  // and unnormalised O_w (rows = queries) in its own LDS region, which only
-  // it has read so far; after one barrier every thread merges, for its rows
-  // and columns, M = max m_w, L = sum 2^(m_w - M) l_w and
-  // O = sum 2^(m_w - M) O_w / L.
+  // ---- combine the waves. Each wave leaves its reference m_w, row sums
+  // (n_w of the rounded P, l_w for the LSE) and unnormalised O_w (rows =
+  // queries) in its own LDS region, which only it has read so far; after one
+  // barrier every thread merges, for its rows and columns, M = max m_w,
+  // O = sum 2^(m_w - M) O_w / sum 2^(m_w - M) n_w and
+  // LSE = ln2 (M + log2 sum 2^(m_w - M) l_w).
   if (half == 0) {
     s_m[wave][r32] = m;  // -inf for a tile with no visible key
     s_l[wave][r32] = l;
+    s_l32[wave][r32] = l32;
   }
   // accumulator registers 4g..4g+3 hold columns 32dt + 8g + 4half .. +3 of
   // the lane's query: one 16-byte store each
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(1024) void fa_fwd_short_kernel(Params p) {
       Mx = vmax(Mx, mw[w]);
     }
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float L = 0.f;
+    float L = 0.f, L32 = 0.f;
 #pragma unroll
     for (int w = 0; w < MAXW; ++w) {
       if (w < nw) {
@@ -250,6 +250,7 @@ __global__ __launch_bounds__(1024) void fa_fwd_short_kernel(Params p) {
         const float* pw = (const float*)(smem + w * REGION) + r * PS + d;
         const f32x4 x0 = *(const f32x4*)pw, x1 = *(const f32x4*)(pw + 4);
         L += f * s_l[w][r];
+        L32 += f * s_l32[w][r];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           acc[i] += f * x0[i];
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(1024) void fa_fwd_short_kernel(Params p) {
       ow[i] = __builtin_bit_cast(uint32_t, M::cvt(acc[2 * i] * inv, acc[2 * i + 1] * inv));
     *(u32x4*)(Oh + (int64_t)(q0 + r) * p.so.n + d) = ow;
     if (p.lse != nullptr && d == 0)
-      p.lse[(size_t)head * Nq + q0 + r] = 0.69314718055994531f * (Mx + log2f(L));
+      p.lse[(size_t)head * Nq + q0 + r] = 0.69314718055994531f * (Mx + log2f(L32));
   }
 }
 

@@ -9,16 +9,19 @@
 // workgroup w takes tiles [w*T/G, (w+1)*T/G) of the T tiles, so every
 // workgroup does the same number of tiles (to within one). A query block cut
 // by such a boundary is computed in pieces, each over its own key range; a
-// piece leaves its unnormalised O, its reference maximum and its row sum, and
-// the combine kernel merges the pieces of a block exactly: with m the largest
-// reference, O = sum_p 2^(m_p - m) O_p / sum_p 2^(m_p - m) l_p. This is the
+// piece leaves its unnormalised O, its reference maximum and its row sums
+// (the normaliser's, n_p, and the log-sum-exp's, l_p; the same sum for
+// fp16), and the combine kernel merges the pieces of a block exactly: with m
+// the largest reference, O = sum_p 2^(m_p - m) O_p / sum_p 2^(m_p - m) n_p
+// and LSE = ln2 (m + log2 sum_p 2^(m_p - m) l_p). This is the
 // same rescaling the online softmax applies between tiles (kwkr.cn YOLO11
 // FlashAttention-2 article, section 1.2), applied across workgroups.
 //
 // Full masks only (every block has the same number of tiles). Workspace per
-// workgroup: two piece slots of BM * (D + 2) floats ([D][BM] O^T, then the
-// BM references and the BM row sums); a workgroup's first and last segments
-// are the only ones that can be pieces.
+// workgroup: two piece slots of BM * (D + 3) floats ([D][BM] O^T, then the
+// BM references, the BM log-sum-exp row sums and the BM normaliser row
+// sums); a workgroup's first and last segments are the only ones that can be
+// pieces.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -29,7 +32,7 @@
 namespace fa {
 
 struct StreamParams {
-  float* part;    // [G][2][BM * (D + 2)] fp32 piece slots
+  float* part;    // [G][2][BM * (D + 3)] fp32 piece slots
   int64_t total;  // T: tiles over all blocks (blocks * ntb)
   int ntb;        // key tiles per query block
   int nblocks;    // B * H * query blocks per head
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_stream_kernel(Params p, Str
     const int qb = bid - head * p.num_qb;
     float* part = nullptr;
     if (t0 != 0 || t1 != sp.ntb)
-      part = sp.part + ((size_t)w * 2 + (first ? 0 : 1)) * (size_t)(BM * (D + 2));
+      part = sp.part + ((size_t)w * 2 + (first ? 0 : 1)) * (size_t)(BM * (D + 3));
     fa_fwd_block<D, BN, NW, RB, S, PIPE, false, T>(p, head, qb, t0, t1, part, smem, vts);
     g += t1 - t0;
     first = false;
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(256) void fa_fwd_combine_kernel(Params p, StreamPar
   // every later workgroup up to wb.
   auto piece = [&](int w) -> const float* {
     const int s = (w == wa && stream_start(sp, wa) < g_first) ? 1 : 0;
-    return sp.part + ((size_t)w * 2 + s) * (size_t)(BM * (D + 2));
+    return sp.part + ((size_t)w * 2 + s) * (size_t)(BM * (D + 3));
   };
   for (int r = threadIdx.x; r < BM; r += 256) {
     const int q_row = qb * BM + r;
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(256) void fa_fwd_combine_kernel(Params p, StreamPar
     float m = -__builtin_inff();
     for (int w = wa; w <= wb; ++w)
       if (has_work(w)) m = vmax(m, piece(w)[D * BM + r]);
-    float l = 0.f;
+    float l = 0.f, n = 0.f;
     float f[MAXP];
     int np = 0;
     for (int w = wa; w <= wb; ++w) {
@@ -130,8 +133,9 @@ __global__ __launch_bounds__(256) void fa_fwd_combine_kernel(Params p, StreamPar
       if (np < MAXP) f[np] = fw;
       ++np;
       l += fw * pc[D * BM + BM + r];
+      n += fw * pc[D * BM + 2 * BM + r];
     }
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / n;
     T* Oh = head_base<T>(p.o, p.so, hb, hh) + (int64_t)q_row * p.so.n;
     for (int d = 0; d < D; d += 2) {
       float a0 = 0.f, a1 = 0.f;

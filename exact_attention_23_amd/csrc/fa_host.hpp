@@ -16,8 +16,9 @@ inline bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   return a0 < b0 + bn && b0 < a0 + an;
 }
 
-// FA_OK for hipSuccess; otherwise records HIP's description of the error for
-// fa_last_launch_error() on this thread and returns FA_ERR_LAUNCH.
+// FA_OK for hipSuccess (the return value of the launch itself); otherwise
+// records HIP's description of the error for fa_last_launch_error() on this
+// thread and returns FA_ERR_LAUNCH.
 int launch_status(hipError_t e);
 
 // Workgroup scheduling shared by the kernels: logical work items are spread

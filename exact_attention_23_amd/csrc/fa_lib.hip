@@ -25,7 +25,9 @@ int device_cus() {
 }
 
 int launch_status(hipError_t e) {
-  if (e == hipSuccess) e = hipGetLastError();
+  // Only the launch's own return value counts: hipGetLastError here would
+  // also pick up (and clear) an error some earlier, unrelated HIP call left
+  // on this thread.
   if (e != hipSuccess) {
     g_launch_error = hipGetErrorString(e);
     return FA_ERR_LAUNCH;

@@ -52,7 +52,7 @@ enum fa_status {
   FA_ERR_ALIGN = 7,   /* a tensor not 16-byte aligned, or lse not 4-byte        */
   FA_ERR_ALIAS = 8,   /* an output overlaps an input, another output or the     */
                       /* workspace                                              */
-  FA_ERR_LAUNCH = 9,  /* the kernel launch itself failed (hipGetLastError)      */
+  FA_ERR_LAUNCH = 9,  /* the kernel launch itself failed (its return value)     */
   FA_ERR_PATH = 10,   /* fa_fwd_ex: unknown path, or FA_PATH_SHORT with Nk too  */
                       /* large for it; fa_bwd_ex: kernel mask not in 1..7       */
   FA_ERR_WORKSPACE = 11, /* fa_bwd: workspace NULL, not 16-byte aligned, or     */
@@ -178,6 +178,10 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
  * aligned, caller-owned, not overlapping any tensor (FA_ERR_WORKSPACE,
  * FA_ERR_ALIAS); its contents on entry do not matter. Two kernels are
  * enqueued on `stream`. Deterministic (fixed split and merge order).
+ * The one exception to "every check before any HIP call": the workspace
+ * size and overlap checks need the number of resident workgroups, which
+ * comes from an occupancy query of the current device (a HIP call that
+ * enqueues nothing); every other check runs before it.
  */
 int64_t fa_fwd_stream_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                                       int dtype);

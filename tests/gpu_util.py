@@ -9,6 +9,7 @@ import torch
 
 import exact_attention_23_amd as fa
 import oracle
+from oracle import pool as oracle_pool
 
 # Tolerances for fp16/bf16 inputs against the fp64 oracle.
 MAX_ABS_O = 1e-2
@@ -37,11 +38,30 @@ def run_gpu(q, k, v, causal, scale=None, with_lse=True, path="auto"):
     return o.cpu(), (lse.cpu() if lse is not None else None)
 
 
-def compare(o_gpu, lse_gpu, O_ref, L_ref, what=""):
-    """Element-wise comparison to the oracle; returns the error summary."""
+# bf16 keeps 8 significant bits: rounding moves a value by at most 2^-8 of
+# itself. Half an ulp of a bf16 output at |O| in [4, 8) is 2^-6 = 0.0156,
+# above the 1e-2 bar, so from |O| = 4 on no bf16 output can be held to it.
+U_BF16 = 2.0 ** -8
+BF16_EXEMPT_ABS_O = 4.0
+
+
+def compare(o_gpu, lse_gpu, O_ref, L_ref, what="", vmax=None):
+    """Element-wise comparison with the oracle at the stated bar: max|dO| <=
+    1e-2, mean|dO| <= 1e-3 and max|dLSE| <= 1e-3, on every element.
+
+    The one exception is bf16 outputs whose reference |O| is 4 or more, where
+    rounding the output alone can exceed 1e-2. Those elements are held to a
+    bound derived from the arithmetic instead: |dO| <= 2^-8 (2|O| + vmax) +
+    1e-5, with vmax = max|V| of the inputs (needed only when such an element
+    misses 1e-2). The terms: the output's rounding (2^-8 |O|) and the rounding
+    of the weights P, which the kernel normalises by the sum of the rounded
+    weights, so the output moves by sum_j w_j d_j (v_j - O) with |d_j| <= 2^-8,
+    at most 2^-8 (sum_j w_j |v_j| + |O|) <= 2^-8 (vmax + |O|); fp32 sums add
+    far less than 1e-5 here. Returns the error summary."""
     og = o_gpu.double().numpy()
-    d = np.abs(og - O_ref)
     assert np.all(np.isfinite(og)), f"{what}: non-finite output"
+    d = np.abs(og - O_ref)
+    absO = np.abs(O_ref)
     max_o, mean_o = float(d.max()), float(d.mean())
     worst = np.unravel_index(int(d.argmax()), d.shape)
     max_l = 0.0
@@ -50,52 +70,29 @@ def compare(o_gpu, lse_gpu, O_ref, L_ref, what=""):
         assert np.all(np.isfinite(lg)), f"{what}: non-finite LSE"
         max_l = float(np.abs(lg - L_ref).max())
     msg = (f"{what}: max|dO|={max_o:.3e} at {tuple(int(x) for x in worst)} "
-           f"(|O|={abs(O_ref[worst]):.3f}) mean|dO|={mean_o:.3e} max|dLSE|={max_l:.3e}")
-    assert max_o <= MAX_ABS_O, msg
+           f"(|O|={absO[worst]:.3f}) mean|dO|={mean_o:.3e} max|dLSE|={max_l:.3e}")
+    if o_gpu.dtype == torch.bfloat16:
+        big = absO >= BF16_EXEMPT_ABS_O
+        small_max = float(d[~big].max()) if (~big).any() else 0.0
+        assert small_max <= MAX_ABS_O, msg + f"; max over |O| < 4: {small_max:.3e}"
+        over = big & (d > MAX_ABS_O)
+        if over.any():
+            assert vmax is not None, msg + ": elements with |O| >= 4 miss 1e-2 and no vmax was given"
+            bound = U_BF16 * (2.0 * absO + float(vmax)) + 1e-5
+            ratio = float((d[over] / bound[over]).max())
+            assert ratio <= 1.0, msg + f"; |O| >= 4 elements reach {ratio:.3f} of their bound"
+    else:
+        assert max_o <= MAX_ABS_O, msg
     assert mean_o <= MEAN_ABS_O, msg
     assert max_l <= MAX_ABS_LSE, msg
     return max_o, mean_o, max_l
 
 
-# The 16-bit matrix instructions' accumulation, relative to sum |a b| (taken
-# as the e4m3 instruction's measured 2^-14.7, rounded up to 2^-13).
-EPS_ACC_16 = 2.0 ** -13
-U_TYPE = {torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}  # half an ulp, relative
-
-
-def compare_derived(o_gpu, lse_gpu, q, k, v, scale, causal, what=""):
-    """Element-wise comparison against a bound derived from the arithmetic,
-    for large logits in bf16, where rounding the output alone can take
-    |dO| past 1e-2 (half an ulp of bf16 at |O| in [2, 4) is 0.0078): per
-    element |dO| <= (u + 2 e) A + u |O| + 1e-5 and |dLSE| <= 1e-3 + e, with u
-    half an ulp of the type (P and O are rounded to it), e = EPS_ACC_16 times
-    the row's largest sum_c |scale q_ic k_jc| (score accumulation), and A the
-    attention output of |V| (which bounds sum_j |dP_ij| |V_jc|)."""
-    O, L = oracle.attention(q, k, v, scale=scale, causal=causal)
-    A, _ = oracle.attention(q, k, v.abs(), scale=scale, causal=causal)
-    B, H = q.shape[:2]
-    M = np.empty(q.shape[:3])
-    for b in range(B):
-        for h in range(H):
-            qa, ka = q[b, h].float().abs().numpy(), k[b, h].float().abs().numpy()
-            S = oracle.scores(qa, ka, abs(scale))
-            M[b, h] = S.max(axis=1)
-    u = U_TYPE[q.dtype]
-    e = EPS_ACC_16 * M[..., None]
-    og = o_gpu.double().numpy()
-    assert np.all(np.isfinite(og)), f"{what}: non-finite output"
-    d = np.abs(og - O)
-    bound = (u + 2 * e) * A + u * np.abs(O) + 1e-5
-    ratio = d / bound
-    worst = np.unravel_index(int(ratio.argmax()), ratio.shape)
-    dl = np.abs(lse_gpu.double().numpy() - L)
-    lratio = dl / (1e-3 + EPS_ACC_16 * M)
-    msg = (f"{what}: worst |dO|/bound={ratio.max():.3f} at {tuple(int(x) for x in worst)} "
-           f"(|dO|={d[worst]:.3e}, bound={bound[worst]:.3e}); max|dO|={d.max():.3e} "
-           f"mean|dO|={d.mean():.3e}; max|dLSE|={dl.max():.3e} (worst ratio {lratio.max():.3f})")
-    assert ratio.max() <= 1.0, msg
-    assert lratio.max() <= 1.0, msg
-    return msg
+def compare_oracle(o_gpu, lse_gpu, q, k, v, scale, causal, what=""):
+    """The whole output of a call against the oracle (run on the host's
+    process pool), at the stated bar (see compare)."""
+    O, L = oracle_pool.attention(q, k, v, scale=scale, causal=causal)
+    return compare(o_gpu, lse_gpu, O, L, what=what, vmax=float(v.float().abs().max()))
 
 
 def rand_inputs(B, H, Nq, Nk, d, dtype, seed, sigma_qk=1.0, v_uniform=False):

@@ -8,18 +8,17 @@ fp64 oracle on the contiguous originals, and the padding around a padded
 output must keep its sentinel. The draws are fixed by the seed, so a failure
 names a reproducible case.
 
-fp16 cases are held to the stated bar (max|dO| <= 1e-2, mean <= 1e-3,
-|dLSE| <= 1e-3). bf16 cases are held to the bound derived from the arithmetic
-(compare_derived) and the stated mean bar: an early causal row sees only a
-few keys, so |O| reaches ~2, where half an ulp of the bf16 output alone is
-0.0078 and the rounded P adds the rest of a 1e-2 excess."""
+Every case is held to the stated bar (max|dO| <= 1e-2, mean <= 1e-3,
+|dLSE| <= 1e-3) on every element; bf16 elements whose reference |O| is 4 or
+more, where half an ulp of the bf16 output alone exceeds 1e-2, are held to
+the bound derived in tests/gpu_util.compare instead."""
 import numpy as np
 import pytest
 import torch
 
 import exact_attention_23_amd as fa
 import oracle
-from tests.gpu_util import compare, compare_derived, default_scale, note, rand_inputs, require_gpu
+from tests.gpu_util import compare, default_scale, note, rand_inputs, require_gpu
 from tests.test_layouts import bnhd_view, padded_rows
 
 pytestmark = pytest.mark.gpu
@@ -68,11 +67,5 @@ def test_random_layout(case):
     if obuf is not None:
         assert bool((obuf[..., c["d"]:] == -7.0).all()), f"{c}: padding of the output was written"
     scale = default_scale(c["d"])
-    if c["dtype"] == "bf16":
-        compare_derived(o.cpu(), lse.cpu(), q, k, v, scale, c["causal"], what=str(c))
-        O, _ = oracle.attention(q, k, v, scale=scale, causal=c["causal"])
-        mean = float(np.abs(o.cpu().double().numpy() - O).mean())
-        assert mean <= 1e-3, f"{c}: mean|dO|={mean:.3e}"
-        return
     O, L = oracle.attention(q, k, v, scale=scale, causal=c["causal"])
-    compare(o.cpu(), lse.cpu(), O, L, what=str(c))
+    compare(o.cpu(), lse.cpu(), O, L, what=str(c), vmax=float(v.float().abs().max()))

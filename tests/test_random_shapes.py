@@ -3,19 +3,17 @@
 kernel drawn at random, each compared element by element with the oracle.
 The draws are fixed by the seed, so a failure names a reproducible case.
 
-fp16 cases are held to the stated bar (max|dO| <= 1e-2, mean <= 1e-3,
-|dLSE| <= 1e-3). bf16 cases are held to the bound derived from the arithmetic
-(compare_derived) and the stated mean bar: logits of several units (a scale
-beyond 1/sqrt(d)) make rows nearly one-hot, and the first rows of a causal
-mask see only a few keys; either way |O| reaches 2-4, where half an ulp of
-the bf16 output alone is 0.0078-0.0156."""
+Every case is held to the stated bar (max|dO| <= 1e-2, mean <= 1e-3,
+|dLSE| <= 1e-3) on every element; bf16 elements whose reference |O| is 4 or
+more, where half an ulp of the bf16 output alone exceeds 1e-2, are held to
+the bound derived in tests/gpu_util.compare instead."""
 import math
 
 import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_util import compare, compare_derived, note, rand_inputs, require_gpu, run_gpu
+from tests.gpu_util import compare, note, rand_inputs, require_gpu, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -48,11 +46,5 @@ def test_random_shape(case):
     q, k, v = rand_inputs(c["B"], c["H"], c["Nq"], c["Nk"], c["d"], c["dtype"], seed=c["seed"])
     o, lse = run_gpu(q, k, v, c["causal"], scale=c["scale"], path=c["path"])
     scale = c["scale"] if c["scale"] is not None else 1.0 / math.sqrt(c["d"])
-    if c["dtype"] == "bf16":
-        compare_derived(o, lse, q, k, v, scale, c["causal"], what=str(c))
-        O, _ = oracle.attention(q, k, v, scale=scale, causal=c["causal"])
-        mean = float(np.abs(o.double().numpy() - O).mean())
-        assert mean <= 1e-3, f"{c}: mean|dO|={mean:.3e}"
-        return
     O, L = oracle.attention(q, k, v, scale=scale, causal=c["causal"])
-    compare(o, lse, O, L, what=str(c))
+    compare(o, lse, O, L, what=str(c), vmax=float(v.float().abs().max()))
