@@ -17,7 +17,7 @@ from ._lib import (FA_DTYPE_BF16, FA_DTYPE_FP16, FA_OK, FA_PATH_AUTO,  # noqa: F
                    FA_PATH_SHORT, FA_PATH_TILED)
 
 __all__ = ["FaError", "fa_fwd", "fa_fwd_ex", "fa_fwd_strided", "attention_fp8", "fa_bwd",
-           "fa_bwd_ex", "fa_bwd_workspace_bytes", "attention", "attention_backward",
+           "fa_bwd_ex", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "attention", "attention_backward",
            "flash_attention", "release_workspaces", "version"]
 
 _PATHS = {"auto": FA_PATH_AUTO, "tiled": FA_PATH_TILED, "short": FA_PATH_SHORT, "stream": -1}
@@ -139,6 +139,16 @@ def fa_bwd_ex(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: 
                                  lse or None, dq or None, dk or None, dv or None,
                                  workspace or None, workspace_bytes, B, H, Nq, Nk, d,
                                  float(scale), int(causal), int(dtype), int(kernels), stream or None)
+
+
+def fa_bwd_noalloc(q: int, k: int, v: int, o: int, dout: int, lse: int, dq: int, dk: int,
+                   dv: int, B: int, H: int, Nq: int, Nk: int, d: int, scale: float, causal: int,
+                   dtype: int, stream: int) -> int:
+    """Direct call of the backward entry point that allocates nothing (its
+    D/LSE records live in the library's static scratch); returns the status."""
+    return _lib.load().fa_bwd_noalloc(q or None, k or None, v or None, o or None, dout or None,
+                                      lse or None, dq or None, dk or None, dv or None, B, H, Nq,
+                                      Nk, d, float(scale), int(causal), int(dtype), stream or None)
 
 
 def _current_stream(device_index: int):

@@ -19,6 +19,8 @@ FA_ERR_LAUNCH = 9
 FA_ERR_PATH = 10
 FA_ERR_WORKSPACE = 11
 FA_ERR_STRIDE = 12
+FA_ERR_SCRATCH = 13
+FA_BWD_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 FA_PATH_AUTO = 0
 FA_PATH_TILED = 1
@@ -85,6 +87,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                               ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     lib.fa_bwd_ex.restype = ctypes.c_int
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+    lib.fa_bwd_noalloc.restype = ctypes.c_int
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_launch_error.argtypes = []

@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/fa.h"
 #include "fa_bwd_kernel.hpp"
 #include "fa_host.hpp"
@@ -60,6 +62,54 @@ BwdKernels pick_bwd(int64_t d, bool causal) {
   }
 }
 
+// The checks of fa_bwd_ex that do not involve the workspace.
+int check_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Nq,
+               int64_t Nk, int64_t d, float scale, int causal, int dtype) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr ||
+      lse == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+    return FA_ERR_NULLPTR;
+  if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (d != 32 && d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t head_lim = (int64_t)1 << 29;
+  if (Nq > head_lim || Nk > head_lim || Nq * d >= head_lim || Nk * d >= head_lim) return FA_ERR_SHAPE;
+  if (B > lim || H > lim || B * H >= lim) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
+       (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u)
+    return FA_ERR_ALIGN;
+  if (((uintptr_t)lse) & 3u) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+// Outputs and the workspace (when not null) are written: none may overlap an
+// input, and they may not overlap each other.
+int check_alias(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, const void* workspace,
+                int64_t ws_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
+  const size_t q_bytes = (size_t)(B * H) * (size_t)(Nq * d) * 2;
+  const size_t kv_bytes = (size_t)(B * H) * (size_t)(Nk * d) * 2;
+  const size_t lse_bytes = (size_t)(B * H) * (size_t)Nq * 4;
+  struct Range {
+    const void* p;
+    size_t n;
+  };
+  const Range inputs[] = {{q, q_bytes}, {k, kv_bytes}, {v, kv_bytes}, {o, q_bytes},
+                          {dout, q_bytes}, {lse, lse_bytes}};
+  const Range written[] = {{dq, q_bytes}, {dk, kv_bytes}, {dv, kv_bytes},
+                           {workspace, workspace != nullptr ? (size_t)ws_bytes : 0}};
+  for (const Range& w : written) {
+    for (const Range& in : inputs)
+      if (fa::overlaps(w.p, w.n, in.p, in.n)) return FA_ERR_ALIAS;
+    for (const Range& w2 : written)
+      if (&w2 != &w && fa::overlaps(w.p, w.n, w2.p, w2.n)) return FA_ERR_ALIAS;
+  }
+  return FA_OK;
+}
+
 hipError_t launch(BwdFn fn, int64_t grid, int threads, fa::BwdParams& p, hipStream_t stream) {
   void* args[] = {&p};
   return hipLaunchKernel((const void*)fn, dim3((unsigned)grid), dim3((unsigned)threads), args, 0, stream);
@@ -89,22 +139,9 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
               int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
               float scale, int causal, int dtype, int kernels, void* stream) {
   // ---- every check happens before the first HIP call
-  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr ||
-      lse == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
-    return FA_ERR_NULLPTR;
-  if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
-  if (d != 32 && d != 64 && d != 128) return FA_ERR_HEADDIM;
-  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  const int st0 = check_args(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, dtype);
+  if (st0 != FA_OK) return st0;
   const int64_t lim = (int64_t)1 << 31;
-  const int64_t head_lim = (int64_t)1 << 29;
-  if (Nq > head_lim || Nk > head_lim || Nq * d >= head_lim || Nk * d >= head_lim) return FA_ERR_SHAPE;
-  if (B > lim || H > lim || B * H >= lim) return FA_ERR_SHAPE;
-  if (causal != 0 && causal != 1) return FA_ERR_CAUSAL;
-  if (!isfinite(scale)) return FA_ERR_SCALE;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
-       (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u)
-    return FA_ERR_ALIGN;
-  if (((uintptr_t)lse) & 3u) return FA_ERR_ALIGN;
   const int64_t ws_need = fa_bwd_workspace_bytes(B, H, Nq);
   if (workspace == nullptr || ((uintptr_t)workspace & 15u) || ws_need < 0 || workspace_bytes < ws_need)
     return FA_ERR_WORKSPACE;
@@ -119,25 +156,8 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
   const int64_t dq_grid = B * H * nqb;
   if (pre_grid >= lim || dkdv_grid >= lim || dq_grid >= lim) return FA_ERR_SHAPE;
 
-  // Outputs and the workspace are written: none may overlap an input, and
-  // they may not overlap each other.
-  const size_t q_bytes = (size_t)(B * H) * (size_t)(Nq * d) * 2;
-  const size_t kv_bytes = (size_t)(B * H) * (size_t)(Nk * d) * 2;
-  const size_t lse_bytes = (size_t)(B * H) * (size_t)Nq * 4;
-  struct Range {
-    const void* p;
-    size_t n;
-  };
-  const Range inputs[] = {{q, q_bytes}, {k, kv_bytes}, {v, kv_bytes}, {o, q_bytes},
-                          {dout, q_bytes}, {lse, lse_bytes}};
-  const Range written[] = {{dq, q_bytes}, {dk, kv_bytes}, {dv, kv_bytes},
-                           {workspace, (size_t)ws_need}};
-  for (const Range& w : written) {
-    for (const Range& in : inputs)
-      if (fa::overlaps(w.p, w.n, in.p, in.n)) return FA_ERR_ALIAS;
-    for (const Range& w2 : written)
-      if (&w2 != &w && fa::overlaps(w.p, w.n, w2.p, w2.n)) return FA_ERR_ALIAS;
-  }
+  const int st1 = check_alias(q, k, v, o, dout, lse, dq, dk, dv, workspace, ws_need, B, H, Nq, Nk, d);
+  if (st1 != FA_OK) return st1;
 
   if (kernels < 1 || kernels > FA_BWD_ALL) return FA_ERR_PATH;
 
@@ -183,6 +203,58 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
     e = launch(ker.dq, dq_grid, ker.dq_threads, p, st);
   }
   return fa::launch_status(e);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// fa_bwd_noalloc: fa_bwd with its D/LSE records in a file-scope device array
+// instead of a caller's workspace, for callers that cannot allocate.
+namespace {
+
+constexpr int64_t kScratchBytes = FA_BWD_NOALLOC_SCRATCH_BYTES;
+
+// One copy per GPU the library runs on, held until the process ends. In host
+// code `scratch` only names the symbol; its device address (per device) comes
+// from hipGetSymbolAddress and is the only form passed to kernels.
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on each device, with that device current), or null on failure.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch[dev].store(ptr, std::memory_order_release);  // the same address for every caller
+  }
+  return ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Nq,
+                   int64_t Nk, int64_t d, float scale, int causal, int dtype, void* stream) {
+  // ---- every check happens before the first HIP call
+  const int st0 = check_args(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, d, scale, causal, dtype);
+  if (st0 != FA_OK) return st0;
+  const int64_t need = fa_bwd_workspace_bytes(B, H, Nq);
+  if (need < 0 || need > kScratchBytes) return FA_ERR_SCRATCH;
+  const int st1 = check_alias(q, k, v, o, dout, lse, dq, dk, dv, nullptr, 0, B, H, Nq, Nk, d);
+  if (st1 != FA_OK) return st1;
+  void* ptr = scratch_ptr();
+  if (ptr == nullptr) return fa::launch_status(hipErrorInvalidSymbol);
+  // The D/LSE pass rewrites every record the other two kernels read (padding
+  // rows included), so nothing left by an earlier call needs clearing.
+  return fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, ptr, kScratchBytes, B, H, Nq, Nk, d, scale,
+                   causal, dtype, FA_BWD_ALL, stream);
 }
 
 }  // extern "C"

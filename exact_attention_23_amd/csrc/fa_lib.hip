@@ -58,6 +58,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_PATH: return "unknown path or kernel selection, or the short path with too many keys for it";
     case FA_ERR_STRIDE: return "strides missing, misaligned, overlapping or too large for one head";
     case FA_ERR_WORKSPACE: return "workspace is null, misaligned or smaller than fa_bwd_workspace_bytes";
+    case FA_ERR_SCRATCH: return "sizes need more than the static scratch of fa_bwd_noalloc (16 MiB)";
     default: return "unknown status";
   }
 }

@@ -57,8 +57,10 @@ enum fa_status {
                       /* large for it; fa_bwd_ex: kernel mask not in 1..7       */
   FA_ERR_WORKSPACE = 11, /* fa_bwd: workspace NULL, not 16-byte aligned, or     */
                          /* smaller than fa_bwd_workspace_bytes                 */
-  FA_ERR_STRIDE = 12  /* fa_fwd_strided: strides NULL, or a layout the kernels  */
+  FA_ERR_STRIDE = 12, /* fa_fwd_strided: strides NULL, or a layout the kernels  */
                       /* cannot address (see fa_fwd_strided)                    */
+  FA_ERR_SCRATCH = 13 /* fa_bwd_noalloc: the sizes need more than the library's */
+                      /* static scratch (FA_BWD_NOALLOC_SCRATCH_BYTES)          */
 };
 
 /* Element types of q, k, v and o (all four share one type). Accumulation is
@@ -297,6 +299,32 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
               const float* lse, void* dq, void* dk, void* dv, void* workspace,
               int64_t workspace_bytes, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
               float scale, int causal, int dtype, int kernels, void* stream);
+
+/*
+ * fa_bwd_noalloc - fa_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same gradients from the same kernels, with the D/LSE
+ * records kept in a scratch array inside the library instead of a
+ * caller-provided workspace. Arguments, results and checks are fa_bwd's
+ * without workspace and workspace_bytes. The caller still provides every
+ * tensor; the library allocates and frees nothing (no hipMalloc, no
+ * allocating library routine).
+ *
+ * The scratch is a static device array of FA_BWD_NOALLOC_SCRATCH_BYTES
+ * (16 MiB), one copy on each GPU the library runs on, held until the process
+ * ends; its address on a device is looked up on the first call on that
+ * device. Sizes with fa_bwd_workspace_bytes(B, H, Nq) above it return
+ * FA_ERR_SCRATCH (e.g. B*H*ceil(Nq/32) > 65536), before any HIP call.
+ * Every call on one GPU shares that GPU's copy: calls that overlap in time
+ * on one GPU (on different streams, or from different threads without
+ * ordering) race and give wrong gradients; calls ordered on one stream are
+ * safe. Nothing in the scratch needs clearing between calls (each call
+ * rewrites every record it reads).
+ */
+#define FA_BWD_NOALLOC_SCRATCH_BYTES (16LL << 20)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Nq,
+                   int64_t Nk, int64_t d, float scale, int causal, int dtype, void* stream);
 
 /* A static, human-readable description of a status code (never NULL). */
 const char* fa_status_str(int status);

@@ -346,3 +346,40 @@ def test_stream_size_queries_reject_bad_sizes():
     assert lib.fa_fwd_stream_workspace_bytes(1, 1, 1, 1, 64, 3) == -1
     assert lib.fa_fwd_stream_advised(16, 4, 6400, 6400, 32, 0, 1) == 0  # causal
     assert lib.fa_fwd_stream_advised(0, 4, 6400, 6400, 32, 0, 0) == 0
+
+
+def ncall(**kw):
+    """fa_bwd_noalloc with BGOOD's arguments (no workspace) overridden by kw."""
+    a = dict(BGOOD)
+    a.update(kw)
+    return fa.fa_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"],
+                             a["dv"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                             a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), _lib.FA_ERR_NULLPTR),
+    (dict(dv=0), _lib.FA_ERR_NULLPTR),
+    (dict(lse=0), _lib.FA_ERR_NULLPTR),
+    (dict(dtype=2), _lib.FA_ERR_DTYPE),
+    (dict(d=96), _lib.FA_ERR_HEADDIM),
+    (dict(Nq=0), _lib.FA_ERR_SHAPE),
+    (dict(causal=2), _lib.FA_ERR_CAUSAL),
+    (dict(scale=float("inf")), _lib.FA_ERR_SCALE),
+    (dict(dq=DQ + 8), _lib.FA_ERR_ALIGN),
+    # the static scratch holds 65536 records of 32 rows: one more is refused
+    (dict(B=1, H=65537, Nq=32), _lib.FA_ERR_SCRATCH),
+    (dict(B=2, H=1, Nq=32 * 32768 + 1), _lib.FA_ERR_SCRATCH),
+    (dict(dq=Q), _lib.FA_ERR_ALIAS),
+    (dict(dv=DK + 256), _lib.FA_ERR_ALIAS),
+])
+def test_noalloc_invalid_arguments_rejected_before_launch(kw, status):
+    assert ncall(**kw) == status
+
+
+def test_noalloc_scratch_limit_matches_header():
+    assert _lib.FA_BWD_NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert re.search(r"#define FA_BWD_NOALLOC_SCRATCH_BYTES \(16LL << 20\)", _header_text())
+    # the largest accepted size fits exactly; checked before any alias test
+    assert fa.fa_bwd_workspace_bytes(1, 65536, 32) == _lib.FA_BWD_NOALLOC_SCRATCH_BYTES
+    assert ncall(B=1, H=65536, Nq=32, dv=DK + 256) == _lib.FA_ERR_ALIAS
