@@ -18,7 +18,7 @@ from ._lib import (FA_DTYPE_BF16, FA_DTYPE_FP16, FA_OK, FA_PATH_AUTO,  # noqa: F
 
 __all__ = ["FaError", "fa_fwd", "fa_fwd_ex", "fa_fwd_strided", "attention_fp8", "fa_bwd",
            "fa_bwd_ex", "fa_bwd_noalloc", "fa_bwd_workspace_bytes", "attention", "attention_backward",
-           "flash_attention", "release_workspaces", "version"]
+           "flash_attention", "release_workspaces", "standard_attention", "fa_std_fwd", "version"]
 
 _PATHS = {"auto": FA_PATH_AUTO, "tiled": FA_PATH_TILED, "short": FA_PATH_SHORT, "stream": -1}
 
@@ -335,6 +335,54 @@ def attention_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float,
             st = lib.fa_fwd_fp8(*call, _current_stream(idx))
     _check(st)
     return out, lse
+
+
+def fa_std_fwd(q: int, k: int, v: int, o: int, lse: Optional[int], s: int, p: int, B: int, H: int,
+               Nq: int, Nk: int, d: int, scale: float, causal: int, dtype: int, stream: int) -> int:
+    """Direct call of the standard-attention entry point; returns the status."""
+    return _lib.load().fa_std_fwd(q or None, k or None, v or None, o or None, lse or None, s or None,
+                                  p or None, B, H, Nq, Nk, d, float(scale), int(causal), int(dtype),
+                                  stream or None)
+
+
+def standard_attention(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
+                       return_intermediates: bool = False):
+    """Attention computed the standard way (the baseline of the fused forward):
+    S = scale Q K^T and P = softmax(S) are materialised in device memory
+    between three kernels. q, k, v as in attention() (contiguous). Returns
+    (out, lse), or (out, lse, s, p) with return_intermediates: s [B, H, Nq,
+    NkP] float32 and p [B, H, Nq, NkP] in q's dtype, NkP = Nk rounded up to
+    a multiple of 64 (columns past Nk: s unwritten, p zero)."""
+    import torch
+
+    _check_gpu_4d(q=q, k=k, v=v)
+    if not (q.device == k.device == v.device) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a device and a dtype")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
+        raise ValueError("k and v must be [B, H, Nk, d] matching q")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lib = _lib.load()
+    nkp = lib.fa_std_row_stride(Nk)
+    if nkp < 0:
+        raise ValueError("Nk out of range")
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    s = torch.empty((B, H, Nq, nkp), dtype=torch.float32, device=q.device)
+    p = torch.empty((B, H, Nq, nkp), dtype=q.dtype, device=q.device)
+    idx = q.device.index
+    call = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), s.data_ptr(),
+            p.data_ptr(), B, H, Nq, Nk, d, float(scale), 1 if causal else 0, code)
+    if idx == torch.cuda.current_device():
+        st = lib.fa_std_fwd(*call, _current_stream(idx))
+    else:
+        with torch.cuda.device(q.device):
+            st = lib.fa_std_fwd(*call, _current_stream(idx))
+    _check(st)
+    return (out, lse, s, p) if return_intermediates else (out, lse)
 
 
 def _check(st: int):

@@ -90,6 +90,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                    ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
     lib.fa_bwd_noalloc.restype = ctypes.c_int
+    lib.fa_std_row_stride.argtypes = [i64]
+    lib.fa_std_row_stride.restype = i64
+    lib.fa_std_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                               ctypes.c_int, ctypes.c_int, vp]
+    lib.fa_std_fwd.restype = ctypes.c_int
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_launch_error.argtypes = []

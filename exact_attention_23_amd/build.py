@@ -18,7 +18,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 ARCH = "gfx950"
-SOURCES = [os.path.join(CSRC, f) for f in ("fa_lib.hip", "fa_api.hip", "fa_bwd.hip", "fa_fp8.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("fa_lib.hip", "fa_api.hip", "fa_bwd.hip", "fa_fp8.hip",
+                                           "fa_std.hip")]
 
 
 def hipcc() -> str:

@@ -326,6 +326,43 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
                    const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Nq,
                    int64_t Nk, int64_t d, float scale, int causal, int dtype, void* stream);
 
+/*
+ * Standard (unfused) attention: the baseline the fused forward is measured
+ * against. The cited articles contrast FlashAttention with attention computed
+ * the standard way ("FlashAttention 深度解读", section 背景: the score matrix
+ * is written to device memory, read back for the softmax, the probabilities
+ * are written and read back again for the product with V; ai2ai.xin
+ * flash-attention-principle page, the five-step list of the self-attention
+ * bottleneck; kwkr.cn YOLO11 FlashAttention-2 article, section 1.1). This
+ * computes the same O and LSE as fa_fwd that way, in three kernels, each a
+ * full pass over an Nq x Nk matrix in HBM:
+ *   1. S = scale * Q K^T      written to s (fp32)
+ *   2. P = softmax_rows(S)    s read, causal mask applied (top-left, as in
+ *                             fa_fwd), p written in dtype, lse written
+ *   3. O = P V                p read
+ * Both products run over the whole Nq x Nk square (causal too), as a
+ * standard implementation does.
+ *
+ * fa_std_row_stride - NkP, the row stride (in elements) of s and p: Nk
+ * rounded up to a multiple of 64; -1 for Nk < 1 or Nk > 2^29.
+ *
+ * fa_std_fwd - arguments as fa_fwd, plus
+ *   s   [B, H, Nq, NkP] fp32, caller-owned device memory, 16-byte aligned:
+ *       s[b,h,i,j] = scale * q_i . k_j for j < Nk (masked entries included);
+ *       columns j >= Nk are not written
+ *   p   [B, H, Nq, NkP] in dtype, caller-owned, 16-byte aligned: the
+ *       normalised attention weights softmax(S) (0 where masked and for
+ *       columns j >= Nk), rounded to dtype; the product with V uses them
+ *       as stored
+ * o, s, p and lse must not overlap an input or each other (FA_ERR_ALIAS).
+ * Additional size limit: Nq * NkP < 2^29 per head (FA_ERR_SHAPE). Three
+ * kernels are enqueued on `stream`. Every check runs before any HIP call.
+ */
+int64_t fa_std_row_stride(int64_t Nk);
+int fa_std_fwd(const void* q, const void* k, const void* v, void* o, float* lse, float* s, void* p,
+               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+               int dtype, void* stream);
+
 /* A static, human-readable description of a status code (never NULL). */
 const char* fa_status_str(int status);
 

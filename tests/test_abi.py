@@ -383,3 +383,42 @@ def test_noalloc_scratch_limit_matches_header():
     # the largest accepted size fits exactly; checked before any alias test
     assert fa.fa_bwd_workspace_bytes(1, 65536, 32) == _lib.FA_BWD_NOALLOC_SCRATCH_BYTES
     assert ncall(B=1, H=65536, Nq=32, dv=DK + 256) == _lib.FA_ERR_ALIAS
+
+
+SS, PP = 0x7000000, 0x8000000  # stand-in device addresses of S and P
+
+
+def stdcall(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, s=SS, p=PP, B=2, H=3, Nq=100, Nk=77, d=64, scale=0.125,
+             causal=0, dtype=0, stream=None)
+    a.update(kw)
+    return fa.fa_std_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["s"], a["p"], a["B"], a["H"],
+                         a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+def test_std_row_stride():
+    assert fa._lib.load().fa_std_row_stride(1) == 64
+    assert fa._lib.load().fa_std_row_stride(64) == 64
+    assert fa._lib.load().fa_std_row_stride(65) == 128
+    assert fa._lib.load().fa_std_row_stride(0) == -1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), _lib.FA_ERR_NULLPTR),
+    (dict(s=0), _lib.FA_ERR_NULLPTR),
+    (dict(p=0), _lib.FA_ERR_NULLPTR),
+    (dict(dtype=3), _lib.FA_ERR_DTYPE),
+    (dict(d=16), _lib.FA_ERR_HEADDIM),
+    (dict(Nk=0), _lib.FA_ERR_SHAPE),
+    (dict(Nq=1 << 16, Nk=1 << 13), _lib.FA_ERR_SHAPE),  # Nq * NkP reaches 2^29
+    (dict(causal=5), _lib.FA_ERR_CAUSAL),
+    (dict(scale=float("nan")), _lib.FA_ERR_SCALE),
+    (dict(s=SS + 4), _lib.FA_ERR_ALIGN),
+    (dict(p=PP + 8), _lib.FA_ERR_ALIGN),
+    (dict(s=Q), _lib.FA_ERR_ALIAS),
+    (dict(p=O), _lib.FA_ERR_ALIAS),
+    (dict(p=SS + 1024), _lib.FA_ERR_ALIAS),
+    (dict(lse=PP), _lib.FA_ERR_ALIAS),
+])
+def test_std_invalid_arguments_rejected_before_launch(kw, status):
+    assert stdcall(**kw) == status
