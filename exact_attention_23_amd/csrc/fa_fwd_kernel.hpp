@@ -37,12 +37,13 @@
 //     16-byte chunks against bank conflicts.
 //   * exp is v_exp_f32 (2^x) on scores scaled by scale*log2(e), folded into one
 //     FMA with the reference maximum. The row sum that normalises O is taken
-//     on the matrix cores (a 16x16x32 MFMA against a 0/1 selector) from the
-//     same rounded P that enters the P V product, so the normalisation
-//     matches the weights actually applied and the vector units are spared.
-//     fp16 takes its log-sum-exp from that sum too; bf16 also sums the fp32 P
+//     from the same rounded P that enters the P V product, so the
+//     normalisation matches the weights actually applied: for fp16 on the
+//     matrix cores (a 16x16x32 MFMA against a 0/1 selector, sparing the
+//     vector units), for bf16 on the vector units (one dot2 per pair). fp16
+//     takes its log-sum-exp from that sum too; bf16 also sums the fp32 P
 //     before rounding for the log-sum-exp, since 8-bit rounding would move it
-//     by up to 2^-9.
+//     by up to 2^-8.
 //   * The reference maximum lags the true running maximum: P of a tile is
 //     formed against it first, and only when that tile's row sum exceeds 2^15
 //     (or is not finite, as on a row's first tile) is the maximum of the tile
@@ -51,7 +52,7 @@
 //     precision; the result is unchanged in exact arithmetic because O and the
 //     row sum carry the same reference. The common path thus needs no row
 //     maximum at all: per score it is one FMA, one exp2 and half a conversion.
-//   * For d <= 64 the block first runs optimistically: the reference comes
+//   * The block first runs optimistically: the reference comes
 //     from its first tile and is never tested again, so no unit waits for its
 //     row sums. A P too large for its type then shows as a non-finite row
 //     sum or output at the end, and the workgroup redoes the block with the
@@ -406,7 +407,7 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
   // operands; returns its row sum of the rounded P, and in l32 (bf16) the
   // lane's fp32 sum of the unrounded P.
   auto exp_unit = [&](const f32x16& sr, float negm, vec (&pr)[2], float& l32) {
-    float lsum = 0.f;
+    float lsum = 0.f, lrnd = 0.f;
     u32x4 w[2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -414,11 +415,13 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[2 * i + 1], c, negm));
       const pair pp = M::cvt(p0, p1);
       lsum = M::lse_sum(p0, p1, lsum);
+      lrnd = M::rnd_sum(pp, lrnd);
       w[i >> 2][i & 3] = __builtin_bit_cast(uint32_t, pp);
     }
     pr[0] = __builtin_bit_cast(vec, w[0]);
     pr[1] = __builtin_bit_cast(vec, w[1]);
     l32 = lsum;
+    if constexpr (M::kVecRowSum) return lrnd;
     return sub_sum(pr);
   };
 
@@ -544,12 +547,13 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
   auto piped_unit = [&](auto mask_tag, int j, int t, f32x16 (&sr)[RB], vec (&pr)[RB][2],
                         float (&ps)[RB], float (&p32)[RB], const vec (&kf)[KS], f32x16 (&sn)[RB]) {
     if (decltype(mask_tag)::value) mask_unit(j, t, sr);
-    float negm[RB], lsum[RB];
+    float negm[RB], lsum[RB], lrnd[RB];
     u32x4 w[RB][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       negm[rb] = -m_run[rb];
       lsum[rb] = 0.f;
+      lrnd[rb] = 0.f;
     }
     [&]<int... I>(std::integer_sequence<int, I...>) {
       (
@@ -564,6 +568,7 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
               const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[rq][2 * i + 1], c, negm[rq]));
               const pair pq = M::cvt(p0, p1);
               lsum[rq] = M::lse_sum(p0, p1, lsum[rq]);
+              lrnd[rq] = M::rnd_sum(pq, lrnd[rq]);
               w[rq][i >> 2][i & 3] = __builtin_bit_cast(uint32_t, pq);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -574,7 +579,10 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
     for (int rb = 0; rb < RB; ++rb) {
       pr[rb][0] = __builtin_bit_cast(vec, w[rb][0]);
       pr[rb][1] = __builtin_bit_cast(vec, w[rb][1]);
-      ps[rb] = sub_sum(pr[rb]);
+      if constexpr (M::kVecRowSum)
+        ps[rb] = lrnd[rb];
+      else
+        ps[rb] = sub_sum(pr[rb]);
       p32[rb] = lsum[rb];
     }
     vec vf[2][NDT];
@@ -667,7 +675,7 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
     bool bad = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float l_tot = l_run[rb] + (M::kLse32 ? l32_run[rb] : 0.f);
+      const float l_tot = l_run[rb] + (M::kLse32 ? l32_run[rb] : 0.f);  // finiteness only
       float om = 0.f;  // bf16 P reaches 2^127 before the row sum overflows: check O too
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
@@ -695,7 +703,8 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int row = wave * WR + 32 * rb + r32;  // row within the block
-      const float l_lse = M::kLse32 ? sum_with_partner(l32_run[rb]) : l_run[rb];
+      const float l_nrm = M::kVecRowSum ? sum_with_partner(l_run[rb]) : l_run[rb];
+      const float l_lse = M::kLse32 ? sum_with_partner(l32_run[rb]) : l_nrm;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -704,7 +713,7 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
       if (half == 0) {
         part[D * BM + row] = m_run[rb];
         part[D * BM + BM + row] = l_lse;
-        part[D * BM + 2 * BM + row] = l_run[rb];
+        part[D * BM + 2 * BM + row] = l_nrm;
       }
     }
     return true;
@@ -714,8 +723,9 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int q_row = wave_q0 + 32 * rb + r32;
-    const float l_lse = M::kLse32 ? sum_with_partner(l32_run[rb]) : l_run[rb];
-    const float inv = 1.0f / l_run[rb];
+    const float l_nrm = M::kVecRowSum ? sum_with_partner(l_run[rb]) : l_run[rb];
+    const float l_lse = M::kLse32 ? sum_with_partner(l32_run[rb]) : l_nrm;
+    const float inv = 1.0f / l_nrm;
     if (q_row < Nq) {
       T* Oh = head_base<T>(p.o, p.so, hb, hh) + (int64_t)q_row * p.so.n;
 #pragma unroll
@@ -752,18 +762,12 @@ __global__ __launch_bounds__(NW * 64, fwd_min_waves(D)) void fa_fwd_kernel(Param
   __shared__ __attribute__((aligned(1024))) char vts[2][BN * D * 2];
   int head, qb;
   work_item<CAUSAL>(p, blockIdx.x, head, qb);
-  if constexpr (D <= 64) {
-    // the optimistic pass, then (rarely) the strict one
+  // the optimistic pass, then (rarely) the strict one
 #pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass)
-      if (fa_fwd_block<D, BN, NW, RB, S, PIPE, CAUSAL, T>(p, head, qb, 0, 0x7fffffff, nullptr, smem,
-                                                          vts, pass == 1))
-        break;
-  } else {
-    // d = 128: the strict pass alone measured faster (the optimistic form
-    // takes a few registers more and saves no wait at this MFMA share)
-    fa_fwd_block<D, BN, NW, RB, S, PIPE, CAUSAL, T>(p, head, qb, 0, 0x7fffffff, nullptr, smem, vts);
-  }
+  for (int pass = 0; pass < 2; ++pass)
+    if (fa_fwd_block<D, BN, NW, RB, S, PIPE, CAUSAL, T>(p, head, qb, 0, 0x7fffffff, nullptr, smem, vts,
+                                                        pass == 1))
+      break;
 }
 
 }  // namespace fa
