@@ -12,8 +12,16 @@ line is printed. The default workload is the batched
 metric also names microseconds per call at N=400, which is measured on the
 20x20-map workload in the same run.
 
-The CPU baseline times the fp64 oracle, unmodified, on a bounded sample of the
-same workload (whole heads, all rows) on the host's cores.
+Beside the headline workload, the line carries a record for every named
+workload (time, TFLOP/s and fraction of the matrix peak, algorithmic and
+measured HBM bytes), the FP8 forward on the two long workloads, the standard
+(unfused) attention against the fused forward on the 2048-token workload, and
+the vector-unit rates of exp2 and FMA with the vector-unit bound they set on
+the d = 32 workload.
+
+The CPU baseline times the fp64 oracle, unmodified, on the host's cores: one
+worker process per core (at most 16), BLAS at one thread each, over whole
+heads of the same workload.
 """
 from __future__ import annotations
 
@@ -42,6 +50,9 @@ BWD_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_23_amd", "csrc", f)
                       for f in ("fa_device.hpp", "fa_bwd_kernel.hpp", "fa_bwd.hip")]
 FP8_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_23_amd", "csrc", f)
                       for f in ("fa_device.hpp", "fa_fwd_kernel.hpp", "fa_fwd_fp8.hpp", "fa_fp8.hip")]
+STD_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_23_amd", "csrc", f)
+                      for f in ("fa_device.hpp", "fa_std_kernel.hpp", "fa_std.hip")]
+STD_KERNELS = ("fa_std_scores_kernel", "fa_std_softmax_kernel", "fa_std_pv_kernel")
 # backward kernels as rocprofv3 names them, and the FA_BWD_* bit of each
 BWD_KERNELS = (("pre", "fa_bwd_pre_kernel", 1), ("dkdv", "fa_bwd_dkdv_kernel", 2),
                ("dq", "fa_bwd_dq_kernel", 4))
@@ -387,8 +398,10 @@ def bwd_record(w, ms: float, per: dict):
 
 def short_stats(w, calls: int = 200):
     """Latency-bound sizes: device time per call (HIP graph of 100 calls),
-    the eager rate, p50/p95 and relative spread of individually event-timed
-    calls, and the algorithmic HBM rate against the 8 TB/s peak."""
+    the eager rate, and the algorithmic HBM rate against the 8 TB/s peak.
+    The launch_plus_event_* figures come from individually event-timed eager
+    calls: they measure the launch and the event pair around each call, not
+    the kernel (its device time is us_per_call_device)."""
     import statistics
 
     import torch
@@ -410,8 +423,9 @@ def short_stats(w, calls: int = 200):
     t = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
     gbs = w.algorithmic_bytes() / (dev_us * 1e-6) / 1e9
     return {"us_per_call_device": round(dev_us, 3), "us_per_call_eager": round(eager_us, 3),
-            "p50_us": round(t[len(t) // 2], 3), "p95_us": round(t[int(len(t) * 0.95)], 3),
-            "std_over_mean": round(statistics.pstdev(t) / statistics.fmean(t), 4),
+            "launch_plus_event_p50_us": round(t[len(t) // 2], 3),
+            "launch_plus_event_p95_us": round(t[int(len(t) * 0.95)], 3),
+            "launch_plus_event_std_over_mean": round(statistics.pstdev(t) / statistics.fmean(t), 4),
             "algorithmic_hbm_gbs": round(gbs, 1),
             "hbm_peak_frac": round(gbs / PEAK_HBM_GBS, 5),
             "tflops": round(w.flops() / (dev_us * 1e-6) / 1e12, 3)}
@@ -448,36 +462,175 @@ def cpu_baseline_bwd(w, budget_s: float = 12.0):
                       f"{dt:.1f} s wall; numpy float64"}
 
 
-def cpu_baseline(w, budget_s: float = 12.0):
-    """The oracle on whole heads of w until ~budget_s of CPU time is spent."""
+def cpu_baseline(w, budget_s: float = 20.0):
+    """The oracle, unmodified, on whole heads of w: one worker process per host
+    core (at most 16), BLAS at one thread each, heads taken 16 at a time until
+    all are done or budget_s has passed. The pool is started and warmed before
+    the clock starts."""
     import numpy as np
 
-    import oracle
+    from oracle import pool
     from workloads import make_inputs
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
     q, k, v = make_inputs(w)
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    rng = np.random.default_rng(0)
-    order = [heads[i] for i in rng.permutation(len(heads))]
-    done = 0
-    t0 = time.perf_counter()
-    for (b, h) in order:
-        oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
-                         scale=w.scale, causal=w.causal)
-        done += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
+    order = [heads[i] for i in np.random.default_rng(0).permutation(len(heads))]
+    with pool.make_executor() as ex:
+        workers = ex._max_workers  # noqa: SLF001
+        pool.warm(ex)
+        done = 0
+        t0 = time.perf_counter()
+        while done < len(order) and time.perf_counter() - t0 < budget_s:
+            chunk = order[done:done + workers]
+            pool.attention_heads(q, k, v, chunk, scale=w.scale, causal=w.causal, executor=ex)
+            done += len(chunk)
+        dt = time.perf_counter() - t0
     flops = w.flops() * done / len(heads)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(workers), "kind": "oracle",
+            "cpu_model": pool.cpu_model(), "host_cores_available": pool.host_cores(),
             "sample": f"{done} of {len(heads)} heads (whole heads, all {w.Nq} query rows) of "
-                      f"{w.name}; {dt:.1f} s wall; numpy float64"}
+                      f"{w.name}; {dt:.1f} s wall; numpy float64, {workers} worker processes, "
+                      f"BLAS at one thread each"}
+
+
+def workload_record(w, steps: int, warmup: int, settle_ms: float):
+    """One named workload's forward: device time per call (events over `steps`
+    back-to-back calls; a replayed HIP graph for the latency-bound sizes),
+    TFLOP/s and fraction of the matrix peak, algorithmic and counter-measured
+    HBM bytes, the latter only when taken on the current kernel source."""
+    latency_bound = w.B * w.H * w.Nq * w.Nk < 10_000_000
+    us = time_graph(w) if latency_bound else time_gpu(w, steps, warmup, settle_ms) * 1e3
+    tflops = w.flops() / (us * 1e-6) / 1e12
+    gbs = w.algorithmic_bytes() / (us * 1e-6) / 1e9
+    traffic = measured_traffic(w.name)
+    rec = {"B": w.B, "H": w.H, "N": w.Nq, "d": w.d, "dtype": w.dtype, "causal": w.causal,
+           "us_per_call": round(us, 3),
+           "timing": "device time per call of a replayed HIP graph" if latency_bound
+           else f"HIP events over {steps} back-to-back calls",
+           "tflops": round(tflops, 3), "mfma_peak_frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
+           "algorithmic_bytes": w.algorithmic_bytes(), "algorithmic_gbs": round(gbs, 1),
+           "hbm_peak_frac": round(gbs / PEAK_HBM_GBS, 5),
+           "traffic_bytes": traffic,
+           "traffic_over_algorithmic": None if traffic is None else round(traffic / w.algorithmic_bytes(), 3)}
+    return rec
+
+
+def fp8_record(w, steps: int, warmup: int, settle_ms: float):
+    ms = time_fp8(w, steps, warmup, settle_ms)
+    tflops = w.flops() / (ms * 1e-3) / 1e12
+    return {"us_per_call": round(ms * 1e3, 3), "tflops": round(tflops, 3),
+            "fp8_mfma_peak_frac": round(tflops / PEAK_MFMA_FP8_TFLOPS, 4),
+            "traffic_bytes": measured_traffic(f"fp8:{w.name}", FP8_KERNEL_SOURCES),
+            "kernel_source_sha": kernel_source_hash(FP8_KERNEL_SOURCES)}
+
+
+def std_vs_fused(w, steps: int = 10, warmup: int = 3):
+    """The standard (unfused) attention against the fused forward on w: ms per
+    call of each, their ratio, and the HBM bytes of each path, algorithmic
+    (the fused forward reads Q, K, V and writes O and LSE once; the standard
+    path also writes and reads S in fp32 and P in the input type) and, when
+    taken on the current sources, measured by the counters."""
+    import torch
+
+    import exact_attention_23_amd as fa
+    from workloads import make_inputs
+
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in make_inputs(w))
+    lib = fa._lib.load()
+    nkp = lib.fa_std_row_stride(w.Nk)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    sbuf = torch.empty((w.B, w.H, w.Nq, nkp), dtype=torch.float32, device=dev)
+    pbuf = torch.empty((w.B, w.H, w.Nq, nkp), dtype=q.dtype, device=dev)
+    stream = fa._current_stream(0)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), sbuf.data_ptr(),
+            pbuf.data_ptr(), w.B, w.H, w.Nq, w.Nk, w.d, float(w.scale), 1 if w.causal else 0,
+            fa._dtype_code(q))
+
+    def std_call():
+        st = lib.fa_std_fwd(*args, stream)
+        if st != 0:
+            raise RuntimeError(fa.status_str(st))
+
+    for _ in range(warmup):
+        std_call()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        std_call()
+    ev1.record()
+    torch.cuda.synchronize()
+    std_ms = ev0.elapsed_time(ev1) / steps
+    o_std = o.clone()
+    fused_ms = time_gpu(w, 4 * steps, warmup, 200.0)
+    o_f, _ = fa.attention(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    diff = float((o_f.float() - o_std.float()).abs().max())
+    del sbuf, pbuf
+    es = 2
+    s_bytes = w.B * w.H * w.Nq * nkp * 4
+    p_bytes = w.B * w.H * w.Nq * nkp * es
+    std_alg = w.algorithmic_bytes() + 2 * s_bytes + 2 * p_bytes
+    return {"workload": w.name, "fused_us": round(fused_ms * 1e3, 3), "standard_us": round(std_ms * 1e3, 3),
+            "standard_over_fused": round(std_ms / fused_ms, 3),
+            "max_abs_diff_of_outputs": diff,
+            "algorithmic_bytes": {"fused": w.algorithmic_bytes(), "standard": std_alg},
+            "standard_passes_over_nq_nk": "S written (fp32), S read, P written (input type), P read",
+            "measured_bytes": {"fused": measured_traffic(w.name),
+                               "standard": measured_traffic(f"std:{w.name}", STD_KERNEL_SOURCES)},
+            "standard_kernel_source_sha": kernel_source_hash(STD_KERNEL_SOURCES)}
+
+
+def vector_rates(iters: int = 4096, blocks: int = 256 * 16):
+    """Chip-wide rates of v_exp_f32, v_fma_f32 and FMA-then-exp2 pairs (the
+    softmax's work per score) from libfa_probe.so: instructions per second
+    and lanes per clock per compute unit at the published 2.4 GHz."""
+    import ctypes
+
+    import torch
+
+    import exact_attention_23_amd as fa
+    from exact_attention_23_amd import build
+
+    lib = ctypes.CDLL(build.PROBE_LIB_PATH)
+    lib.fa_probe_vector_rate.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_probe_vector_rate.restype = ctypes.c_int
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    stream = fa._current_stream(0)
+    res = {}
+    for name, op in (("exp2", 0), ("fma", 1), ("fma_exp2_pair", 2)):
+        for _ in range(2):  # warm up the clock
+            assert lib.fa_probe_vector_rate(op, blocks, iters, 8, out.data_ptr(), stream) == 0
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        reps = 3
+        for _ in range(reps):
+            assert lib.fa_probe_vector_rate(op, blocks, iters, 8, out.data_ptr(), stream) == 0
+        ev1.record()
+        torch.cuda.synchronize()
+        sec = ev0.elapsed_time(ev1) * 1e-3 / reps
+        instr = blocks * 4 * iters * 8  # wave64 instructions (4 waves per workgroup)
+        res[name] = {"wave_instr_per_s": instr / sec,
+                     "lanes_per_clk_per_cu_at_2p4ghz": round(instr * 64 / sec / (256 * 2.4e9), 2)}
+    if not torch.isfinite(out).all():
+        raise RuntimeError("probe produced non-finite values")
+    return res
+
+
+def vector_roofline(w, us: float, rates):
+    """The vector-unit bound of the forward on w: per score the softmax needs
+    one FMA and one exp2 (the pair the probe times), so the pairs of all
+    scores at the probed pair rate take `floor_us`; the measured time is
+    reported as a fraction of that bound (1 = at the bound). Conversions,
+    row sums and masking are left out, so the bound is optimistic."""
+    scores = w.B * w.H * w.Nq * w.Nk / (2 if w.causal else 1)
+    pair_lanes_per_s = rates["fma_exp2_pair"]["wave_instr_per_s"] * 64
+    floor_us = scores / pair_lanes_per_s * 1e6
+    return {"bound": "valu (exp2 + fma per score)", "floor_us": round(floor_us, 2),
+            "achieved_us": round(us, 3), "frac": round(floor_us / us, 4)}
 
 
 def copy_calibration(mib: int, reps: int = 5):
@@ -512,40 +665,56 @@ def _counter_rows(csv_dir: str, counter: str):
 
 def write_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str,
                   copy_write_dir: str, copy_mib: int, command: str, bwd: bool = False,
-                  fp8: bool = False):
+                  fp8: bool = False, std: bool = False):
     """Record HBM bytes per launch of the attention kernel (the forward, or
-    with bwd the dK/dV kernel of the backward, keyed "bwd:<workload>") from
-    rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch), each scaled by
-    what the same counter reads for a plain copy of copy_mib MiB (known bytes)."""
+    with bwd the dK/dV kernel of the backward, keyed "bwd:<workload>"; with
+    std the three kernels of the standard attention summed per call, keyed
+    "std:<workload>") from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per
+    dispatch), each scaled by what the same counter reads for a plain copy of
+    copy_mib MiB (known bytes)."""
     import statistics
 
     known = copy_mib * (1 << 20)
     cf = [v for k, v in _counter_rows(copy_fetch_dir, "FETCH_SIZE") if "copyBuffer" in k or "copy" in k.lower()]
     cw = [v for k, v in _counter_rows(copy_write_dir, "WRITE_SIZE") if "copyBuffer" in k or "copy" in k.lower()]
-    kname = "fa_bwd_dkdv_kernel" if bwd else ("fa_fwd_fp8_kernel" if fp8 else "fa_fwd_kernel")
-    kf = [v for k, v in _counter_rows(fetch_dir, "FETCH_SIZE") if kname in k]
-    kw = [v for k, v in _counter_rows(write_dir, "WRITE_SIZE") if kname in k]
-    if not (cf and cw and kf and kw):
-        raise RuntimeError("missing counter rows")
-    f_scale = known / (statistics.median(cf) * 1024)
-    w_scale = known / (statistics.median(cw) * 1024)
-    fetch = statistics.median(kf) * 1024 * f_scale
-    write = statistics.median(kw) * 1024 * w_scale
+    f_scale = known / (statistics.median(cf) * 1024) if cf else None
+    w_scale = known / (statistics.median(cw) * 1024) if cw else None
+    if std:
+        kname = "+".join(STD_KERNELS)
+        fetch = write = 0.0
+        for kn in STD_KERNELS:
+            kf = [v for k, v in _counter_rows(fetch_dir, "FETCH_SIZE") if kn in k]
+            kw = [v for k, v in _counter_rows(write_dir, "WRITE_SIZE") if kn in k]
+            if not (cf and cw and kf and kw):
+                raise RuntimeError(f"missing counter rows for {kn}")
+            fetch += statistics.median(kf) * 1024 * f_scale
+            write += statistics.median(kw) * 1024 * w_scale
+    else:
+        kname = "fa_bwd_dkdv_kernel" if bwd else ("fa_fwd_fp8_kernel" if fp8 else "fa_fwd_kernel")
+        kf = [v for k, v in _counter_rows(fetch_dir, "FETCH_SIZE") if kname in k]
+        kw = [v for k, v in _counter_rows(write_dir, "WRITE_SIZE") if kname in k]
+        if not (cf and cw and kf and kw):
+            raise RuntimeError("missing counter rows")
+        fetch = statistics.median(kf) * 1024 * f_scale
+        write = statistics.median(kw) * 1024 * w_scale
     try:
         with open(TRAFFIC_FILE, encoding="utf-8") as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         rec = {}
     rec["about"] = ("HBM bytes per launch of fa_fwd_kernel (key: workload), of "
-                    "fa_bwd_dkdv_kernel (key: bwd:workload) and of fa_fwd_fp8_kernel (key: "
-                    "fp8:workload) from rocprofv3 FETCH_SIZE and "
+                    "fa_bwd_dkdv_kernel (key: bwd:workload), of fa_fwd_fp8_kernel (key: "
+                    "fp8:workload) and per call of the three standard-attention kernels (key: "
+                    "std:workload) from rocprofv3 FETCH_SIZE and "
                     "WRITE_SIZE (KiB per dispatch), scaled by the same counters on a plain "
                     "device copy of known size. Written by bench.py --write-traffic.")
-    key = f"bwd:{workload}" if bwd else (f"fp8:{workload}" if fp8 else workload)
+    key = f"bwd:{workload}" if bwd else (f"fp8:{workload}" if fp8 else
+                                         (f"std:{workload}" if std else workload))
     rec.setdefault("workloads", {})[key] = {
         "kernel": kname,
         "kernel_source_sha": kernel_source_hash(BWD_KERNEL_SOURCES if bwd else
-                                                (FP8_KERNEL_SOURCES if fp8 else None)),
+                                                (FP8_KERNEL_SOURCES if fp8 else
+                                                 (STD_KERNEL_SOURCES if std else None))),
         "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
         "hbm_bytes_per_launch": round(fetch + write),
         "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
@@ -583,6 +752,12 @@ def main(argv=None):
     ap.add_argument("--fp8", action="store_true",
                     help="forward on the workload's inputs quantised to e4m3 (fa_fwd_fp8), "
                          "against the fp8 matrix peak")
+    ap.add_argument("--std", action="store_true",
+                    help="a line for the standard (unfused) attention against the fused forward "
+                         "on --workload only")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="leave out the per-workload, FP8, standard-attention and vector-rate "
+                         "sections of the forward line")
     ap.add_argument("--layout", choices=("bhnd", "bnhd", "qkv"), default="bhnd",
                     help="memory layout of q, k, v, o for the forward: contiguous [B,H,N,d] "
                          "(default), sequence-major [B,N,H,d], or views of a fused [B,N,3,H,d] "
@@ -591,7 +766,7 @@ def main(argv=None):
     if args.write_traffic:
         fd, wd, cfd, cwd, mib = args.write_traffic
         print(json.dumps(write_traffic(args.workload, fd, wd, cfd, cwd, int(mib), args.command,
-                                       bwd=args.which == "bwd", fp8=args.fp8)))
+                                       bwd=args.which == "bwd", fp8=args.fp8, std=args.std)))
         return 0
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
@@ -602,9 +777,19 @@ def main(argv=None):
               "single-GPU kernel at a fraction of the heads.", file=sys.stderr)
         return 2
 
-    from workloads import WORKLOADS
+    from workloads import WORKLOAD_ORDER, WORKLOADS
 
     w = WORKLOADS[args.workload]
+    if args.std:
+        rec = std_vs_fused(w, max(args.steps // 5, 2), max(args.warmup // 3, 1))
+        line = {"metric": "standard (unfused) attention against the fused forward, us per call",
+                "value": rec["standard_us"], "unit": "us", "n_gpus": 1, "steps": args.steps,
+                "warmup": args.warmup, "ms_per_step": rec["standard_us"] * 1e-3,
+                "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+                "dtype": w.dtype, "data": "synthetic", "config": {"workload": w.name},
+                "standard_vs_fused": rec}
+        print(json.dumps(line), flush=True)
+        return 0
     if args.which == "bwd":
         ms, per = time_bwd(w, args.steps, args.warmup, args.settle_ms)
         rec = bwd_record(w, ms, per)
@@ -693,6 +878,21 @@ def main(argv=None):
         "algorithmic_hbm_gbs": round(w.algorithmic_bytes() / (ms * 1e-3) / 1e9, 1),
         "kernel_source_sha": kernel_source_hash(),
     }
+    if not args.no_extras:
+        # every named workload (the headline above is one of them), the FP8
+        # forward of the two long ones, the standard attention against the
+        # fused forward, and the vector-unit bound of the headline workload
+        line["workloads"] = {n: workload_record(WORKLOADS[n], args.steps, args.warmup, args.settle_ms)
+                             for n in WORKLOAD_ORDER}
+        if not args.no_clock:
+            line["workloads"]["long16k"]["clock_mhz_under_load"] = clock_under_load(WORKLOADS["long16k"])
+            line["workloads"]["seq2048"]["clock_mhz_under_load"] = clock_under_load(WORKLOADS["seq2048"])
+        line["fp8"] = {n: fp8_record(WORKLOADS[n], args.steps, args.warmup, args.settle_ms)
+                       for n in ("seq2048", "long16k")}
+        line["standard_vs_fused"] = std_vs_fused(WORKLOADS["seq2048"])
+        rates = vector_rates()
+        line["vector_rates"] = rates
+        line["vector_roofline"] = vector_roofline(w, ms * 1e3, rates)
     if not args.no_bwd:
         # the backward pass of the same workload (a separate figure: the
         # headline value above is the forward's)

@@ -1,0 +1,41 @@
+/*
+ * fa_probe.h - C ABI of libfa_probe.so, a measurement aid that is not part of
+ * the attention library: the vector-unit throughput of the instructions the
+ * forward's softmax step spends its time on (exp2 and fused multiply-add, the
+ * per-score work of the online softmax in "FlashAttention 深度解读", section
+ * 原理 2, and the kwkr.cn YOLO11 FlashAttention-2 article, section 1.2). The
+ * benchmark turns the measured rates into a vector-unit bound for the
+ * forward next to its matrix-core bound.
+ *
+ * fa_probe_vector_rate - enqueue one kernel on `stream` that runs `iters`
+ * iterations of `chains` independent dependency chains per thread, each
+ * iteration one instruction per chain of the kind `op` selects:
+ *   FA_PROBE_EXP2 (0)  v_exp_f32 (2^x)
+ *   FA_PROBE_FMA  (1)  v_fma_f32
+ *   FA_PROBE_MIX  (2)  one v_fma_f32 feeding one v_exp_f32 (the softmax's
+ *                      pair per score; counted as one pair)
+ * over `blocks` workgroups of 256 threads. Each thread writes one float of
+ * its final values to out[blocks * 256] (device memory, caller-owned), so
+ * nothing is optimised away. The instruction count is blocks * 256 * iters *
+ * chains. Returns 0, or 1 for invalid arguments (op outside 0..2, blocks or
+ * iters < 1, chains not 8, out NULL), or 2 when the launch fails. Time it
+ * with events on `stream`.
+ */
+#ifndef FA_PROBE_H_
+#define FA_PROBE_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_probe_op { FA_PROBE_EXP2 = 0, FA_PROBE_FMA = 1, FA_PROBE_MIX = 2 };
+
+int fa_probe_vector_rate(int op, int blocks, int iters, int chains, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_PROBE_H_ */

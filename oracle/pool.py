@@ -82,13 +82,33 @@ def _as_array(t) -> np.ndarray:
     return np.asarray(t)
 
 
+def make_executor(workers: Optional[int] = None) -> ProcessPoolExecutor:
+    """A pool of spawned workers, one per host core up to MAX_WORKERS (or
+    `workers`), each with its BLAS library at one thread."""
+    n = min(workers or MAX_WORKERS, host_cores(), MAX_WORKERS)
+    return ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn"),
+                               initializer=_init_worker)
+
+
+def warm(executor: ProcessPoolExecutor) -> None:
+    """Start every worker of `executor` (spawning and importing happen here)."""
+    n = executor._max_workers  # noqa: SLF001 - the size the pool was made with
+    list(executor.map(_noop, range(4 * n), chunksize=1))
+
+
+def _noop(_):
+    return 0
+
+
 def attention_heads(q, k, v, heads: Sequence[Tuple[int, int]], scale: Optional[float] = None,
                     causal: bool = False, rows: Optional[Iterable[int]] = None,
-                    row_block: int = 1024, workers: Optional[int] = None):
+                    row_block: int = 1024, workers: Optional[int] = None,
+                    executor: Optional[ProcessPoolExecutor] = None):
     """Oracle O and LSE of the listed heads (b, h) of [B, H, N, d] inputs.
 
     rows: the query rows to compute (all rows by default), taken row_block
-    at a time. Returns (O, L): O [len(heads), len(rows), d] and
+    at a time. executor: a pool from make_executor to run on (else one is
+    made for this call). Returns (O, L): O [len(heads), len(rows), d] and
     L [len(heads), len(rows)] in float64, in the order given.
     """
     d = q.shape[-1]
@@ -107,14 +127,16 @@ def attention_heads(q, k, v, heads: Sequence[Tuple[int, int]], scale: Optional[f
             tasks.append(((hi, r0), qh[rr], kh, vh, scale, causal, rr))
     O = np.empty((len(heads), len(rows), d))
     L = np.empty((len(heads), len(rows)))
+    if executor is not None:
+        for (hi, r0), o, l in executor.map(_run, tasks, chunksize=1):
+            O[hi, r0:r0 + o.shape[0]], L[hi, r0:r0 + o.shape[0]] = o, l
+        return O, L
     if n <= 1 or len(tasks) == 1:
         results = map(_run, tasks)
         for (hi, r0), o, l in results:
             O[hi, r0:r0 + o.shape[0]], L[hi, r0:r0 + o.shape[0]] = o, l
         return O, L
-    ctx = mp.get_context("spawn")
-    with ProcessPoolExecutor(max_workers=min(n, len(tasks)), mp_context=ctx,
-                             initializer=_init_worker) as ex:
+    with make_executor(min(n, len(tasks))) as ex:
         for (hi, r0), o, l in ex.map(_run, tasks, chunksize=1):
             O[hi, r0:r0 + o.shape[0]], L[hi, r0:r0 + o.shape[0]] = o, l
     return O, L
