@@ -692,6 +692,9 @@ def write_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir:
     else:
         kname = "fa_bwd_dkdv_kernel" if bwd else ("fa_fwd_fp8_kernel" if fp8 else "fa_fwd_kernel")
         kf = [v for k, v in _counter_rows(fetch_dir, "FETCH_SIZE") if kname in k]
+        if not kf and not (bwd or fp8):  # a latency-bound size runs the short-range kernel
+            kname = "fa_fwd_short_kernel"
+            kf = [v for k, v in _counter_rows(fetch_dir, "FETCH_SIZE") if kname in k]
         kw = [v for k, v in _counter_rows(write_dir, "WRITE_SIZE") if kname in k]
         if not (cf and cw and kf and kw):
             raise RuntimeError("missing counter rows")
