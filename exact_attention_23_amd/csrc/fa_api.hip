@@ -24,27 +24,35 @@ struct Variant {
 };
 
 // Tile shapes per head width: NW waves of RB 32-row blocks, BN keys per tile,
-// S LDS stages, and whether the software-pipelined loop is used.
-template <int D, int BN, int NW, int RB, int S, bool PIPE, typename T>
+// S LDS stages, whether the software-pipelined loop is used, and whether V^T
+// goes through a transposed LDS copy (VT = 1) or is read from the V tile
+// directly (VT = 0).
+template <int D, int BN, int NW, int RB, int S, bool PIPE, int VT, typename T>
 Variant make_variant(bool causal) {
   Variant v;
-  v.fn = causal ? fa::fa_fwd_kernel<D, BN, NW, RB, S, PIPE, true, T>
-                : fa::fa_fwd_kernel<D, BN, NW, RB, S, PIPE, false, T>;
+  v.fn = causal ? fa::fa_fwd_kernel<D, BN, NW, RB, S, PIPE, VT, true, T>
+                : fa::fa_fwd_kernel<D, BN, NW, RB, S, PIPE, VT, false, T>;
   v.bm = 32 * RB * NW;
   v.threads = 64 * NW;
   return v;
 }
 
-// Tile configuration per head width as (D, BN, NW, RB, S, PIPE). A build
+// Tile configuration per head width as (D, BN, NW, RB, S, PIPE, VT). A build
 // can override them with -DFA_TILES_D32=... etc. to compare configurations.
+// All three read V^T straight from the V tiles (VT = 0); measured against the
+// transposed copy (same box, interleaved): 470 vs 480 us (yolo80b16), 2129
+// vs 2148 us (long16k). At d = 64 the smaller LDS footprint (48 KB with a
+// 3-stage ring) lets three 4-wave workgroups of one 32-row block per wave
+// share a CU (155 registers): 409 vs 417 us on seq2048, the same as two
+// row blocks per wave at two workgroups per CU, without its spills.
 #ifndef FA_TILES_D32
-#define FA_TILES_D32 32, 64, 4, 2, 4, true
+#define FA_TILES_D32 32, 64, 4, 2, 4, true, 0
 #endif
 #ifndef FA_TILES_D64
-#define FA_TILES_D64 64, 64, 4, 2, 4, false
+#define FA_TILES_D64 64, 64, 4, 1, 3, false, 0
 #endif
 #ifndef FA_TILES_D128
-#define FA_TILES_D128 128, 64, 8, 1, 4, false
+#define FA_TILES_D128 128, 64, 8, 1, 4, false, 0
 #endif
 
 template <typename T>
@@ -62,9 +70,9 @@ struct StreamVariant {
   StreamFn fn, combine;
   int bm, threads;
 };
-template <int D, int BN, int NW, int RB, int S, bool PIPE, typename T>
+template <int D, int BN, int NW, int RB, int S, bool PIPE, int VT, typename T>
 StreamVariant make_stream() {
-  return {fa::fa_fwd_stream_kernel<D, BN, NW, RB, S, PIPE, T>,
+  return {fa::fa_fwd_stream_kernel<D, BN, NW, RB, S, PIPE, VT, T>,
           fa::fa_fwd_combine_kernel<D, 32 * RB * NW, T>, 32 * RB * NW, 64 * NW};
 }
 template <typename T>

@@ -148,10 +148,17 @@ __device__ __forceinline__ void work_item(const Params& p, int bid, int& head, i
 // raises the reference whenever a unit's row sum exceeds 2^15 or is not
 // finite, so P never overflows. (A runtime flag, not a template parameter:
 // one copy of the loop serves both passes.)
-template <int D, int BN, int NW, int RB, int S, bool PIPE, bool CAUSAL, typename T>
+//
+// VT = 1: each V tile is transposed once per workgroup into a double-buffered
+// V^T tile (vts, 2 x BN*D*2 bytes), which the waves read with 16-byte reads.
+// VT = 0: no V^T buffer (vts unused); every wave reads its V^T operands from
+// the V tile itself with transpose reads (two per operand), which saves the
+// transpose step, its barrier distance and its LDS, so the ring can be
+// shorter (S >= 2, or 3 with PIPE).
+template <int D, int BN, int NW, int RB, int S, bool PIPE, int VT, bool CAUSAL, typename T>
 __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, int t_lo, int t_hi,
                                              float* part, char (&smem)[S][2][BN * D * 2],
-                                             char (&vts)[2][BN * D * 2], bool strict = true) {
+                                             char* vts, bool strict = true) {
   using M = Mma<T>;
   using vec = typename M::vec;
   using pair = typename M::pair;
@@ -171,10 +178,13 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
   static_assert(CPT >= 1 && CPT * NT == CHUNKS, "tile must split evenly over threads");
   static_assert(TPW >= 1 && TPW * 4 * NW == TBLK, "V transpose must split evenly over waves");
   static_assert(BM % BN == 0, "a query block must cover whole key tiles");
-  // Loads left in flight at the end of an iteration: the next iteration reads
-  // K of tile j+1 and transposes V of tile j+2, so those must have landed.
-  constexpr int PENDING = (S - 3) * LOADS;
-  static_assert(S >= 3 && PENDING < 64, "stage count out of range");
+  // Loads left in flight at the end of an iteration. VT = 1: the next
+  // iteration reads K of tile j+1 (and, pipelined, of j+2) and transposes V
+  // of tile j+2, so tiles up to j+2 must have landed. VT = 0: it reads K and
+  // V of tile j+1 (pipelined: also K of j+2).
+  constexpr int AHEAD = VT ? 3 : (PIPE ? 3 : 2);
+  constexpr int PENDING = (S - AHEAD) * LOADS;
+  static_assert(S >= AHEAD && PENDING < 64, "stage count out of range");
 
 
   int tid = threadIdx.x;
@@ -320,16 +330,36 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
       for (int s2 = 0; s2 < 2; ++s2)
         v_roff[dt][t][s2] = lds_off<2 * BN>(32 * dt + r32, 4 * t + 2 * half + s2);
 
-  // V tile j (as loaded) -> V^T buffer j % 2
+  // V tile j (as loaded) -> V^T buffer j % 2 (VT = 1 only)
   auto transpose_v = [&](int j) {
-    const char* vsrc = smem[(j - t_lo) % S][1];
-    char* vdst = vts[(j - t_lo) & 1];
-    i16x4 blk[TPW];
+    if constexpr (VT != 0) {
+      const char* vsrc = smem[(j - t_lo) % S][1];
+      char* vdst = vts + ((j - t_lo) & 1) * TILE_BYTES;
+      i16x4 blk[TPW];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i)
-      blk[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vsrc + tr_src[i]));
+      for (int i = 0; i < TPW; ++i)
+        blk[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vsrc + tr_src[i]));
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) *(i16x4*)(vdst + tr_dst[i]) = blk[i];
+      for (int i = 0; i < TPW; ++i) *(i16x4*)(vdst + tr_dst[i]) = blk[i];
+    }
+  };
+  // VT = 0: the V^T operand for d tile dt and keys k0 .. k0+7 (k0 = 32t +
+  // 16*half + 8*s2) straight from the V tile: two transpose reads, each
+  // handing lane x of a 16-lane group keys k0..k0+3 (then k0+4..k0+7) of d
+  // column 32dt + 16*((lane/16)%2) + x while pointing at key k0 + x/4,
+  // columns d0 + 4*(x%4)..+3 (all lanes of a group share k0 and d0).
+  const int trx = lane & 15;
+  const int tr_row = 16 * half + (trx >> 2);                    // key row of the first read, t = s2 = 0
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (trx & 3);    // d column, dt = 0
+  auto vt_direct = [&](const char* vs, int t, int s2, int dt) -> vec {
+    const int row = tr_row + 32 * t + 8 * s2;
+    const int col = tr_col + 32 * dt;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(vs + lds_off<2 * D>(row, col >> 3) + 2 * (col & 7)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(vs + lds_off<2 * D>(row + 4, col >> 3) + 2 * (col & 7)));
+    const u32x2 wl = __builtin_bit_cast(u32x2, lo), wh = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(vec, u32x4{wl[0], wl[1], wh[0], wh[1]});
   };
 
   // The work is a sequence of units, one per 32-key subtile t of tile j
@@ -358,11 +388,19 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
     for (int s = 0; s < KS; ++s) kf[s] = *(const vec*)(ks + k_roff[t][s]);
   };
   auto load_v = [&](int j, int t, vec (&vf)[2][NDT]) {
-    const char* vs = vts[(j - t_lo) & 1];
+    if constexpr (VT != 0) {
+      const char* vs = vts + ((j - t_lo) & 1) * TILE_BYTES;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) vf[s2][dt] = *(const vec*)(vs + v_roff[dt][t][s2]);
+        for (int dt = 0; dt < NDT; ++dt) vf[s2][dt] = *(const vec*)(vs + v_roff[dt][t][s2]);
+    } else {
+      const char* vs = smem[(j - t_lo) % S][1];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) vf[s2][dt] = vt_direct(vs, t, s2, dt);
+    }
   };
   auto qk = [&](const vec (&kf)[KS], f32x16 (&out)[RB]) {
 #pragma unroll
@@ -620,8 +658,10 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
   for (int t = 0; t < S - 1; ++t) issue(t_lo + t);
   wait_vmcnt<PENDING>();
   __syncthreads();
-  transpose_v(t_lo);
-  __syncthreads();
+  if constexpr (VT != 0) {
+    transpose_v(t_lo);
+    __syncthreads();
+  }
 
   // Causal: a tile whose first key comes after this wave's last row adds
   // nothing to any of its rows, and neither does any later tile. The test is
@@ -746,27 +786,37 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
   return true;
 }
 
-// Waves per SIMD the register allocation must allow. At d = 64 two
-// workgroups share a CU by LDS (80 KB each), and the bf16 form (fp32 row
-// sums on the vector units) would otherwise take a few registers more than
-// half the file and run one wave per SIMD; capped, it spills about a dozen
-// registers and runs 15% faster.
-constexpr int fwd_min_waves(int d) { return d == 64 ? 2 : 1; }
+// Waves per SIMD the register allocation must allow. At d = 64 with a V^T
+// copy, two workgroups share a CU by LDS (80 KB each), and the bf16 form would
+// otherwise take a few registers more than half the file; capped at two
+// waves it spills a dozen registers and runs 15% faster. Reading V^T
+// directly, three workgroups share a CU (48 KB each) and the cap is three
+// waves (one 32-row block per wave needs about 155 registers).
+#ifndef FA_FWD_MIN_WAVES_D64_DIRECT
+#define FA_FWD_MIN_WAVES_D64_DIRECT 3
+#endif
+constexpr int fwd_min_waves(int d, int vt) {
+  return d == 64 ? (vt ? 2 : FA_FWD_MIN_WAVES_D64_DIRECT) : 1;
+}
 
-template <int D, int BN, int NW, int RB, int S, bool PIPE, bool CAUSAL, typename T>
-__global__ __launch_bounds__(NW * 64, fwd_min_waves(D)) void fa_fwd_kernel(Params p) {
-  // K and V tiles as loaded ([stage][K,V], rows = keys), and V^T tiles
-  // (rows = d, BN keys each) for the P V operand, double-buffered: while
-  // tile j runs, V^T of tile j+1 is written.
+template <int D, int BN, int NW, int RB, int S, bool PIPE, int VT, bool CAUSAL, typename T>
+__global__ __launch_bounds__(NW * 64, fwd_min_waves(D, VT)) void fa_fwd_kernel(Params p) {
+  // K and V tiles as loaded ([stage][K,V], rows = keys), and (VT = 1) V^T
+  // tiles (rows = d, BN keys each) for the P V operand, double-buffered:
+  // while tile j runs, V^T of tile j+1 is written.
   __shared__ __attribute__((aligned(1024))) char smem[S][2][BN * D * 2];
-  __shared__ __attribute__((aligned(1024))) char vts[2][BN * D * 2];
   int head, qb;
   work_item<CAUSAL>(p, blockIdx.x, head, qb);
+  char* vts = nullptr;
+  if constexpr (VT != 0) {
+    __shared__ __attribute__((aligned(1024))) char vt_buf[2][BN * D * 2];
+    vts = &vt_buf[0][0];
+  }
   // the optimistic pass, then (rarely) the strict one
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass)
-    if (fa_fwd_block<D, BN, NW, RB, S, PIPE, CAUSAL, T>(p, head, qb, 0, 0x7fffffff, nullptr, smem, vts,
-                                                        pass == 1))
+    if (fa_fwd_block<D, BN, NW, RB, S, PIPE, VT, CAUSAL, T>(p, head, qb, 0, 0x7fffffff, nullptr, smem,
+                                                            vts, pass == 1))
       break;
 }
 

@@ -45,11 +45,15 @@ __device__ __forceinline__ int64_t stream_start(const StreamParams& sp, int w) {
   return (int64_t)w * sp.total / sp.G;
 }
 
-template <int D, int BN, int NW, int RB, int S, bool PIPE, typename T>
+template <int D, int BN, int NW, int RB, int S, bool PIPE, int VT, typename T>
 __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_stream_kernel(Params p, StreamParams sp) {
   constexpr int BM = 32 * RB * NW;
   __shared__ __attribute__((aligned(1024))) char smem[S][2][BN * D * 2];
-  __shared__ __attribute__((aligned(1024))) char vts[2][BN * D * 2];
+  char* vts = nullptr;
+  if constexpr (VT != 0) {
+    __shared__ __attribute__((aligned(1024))) char vt_buf[2][BN * D * 2];
+    vts = &vt_buf[0][0];
+  }
   // Logical numbering: workgroups are dispatched round-robin over the 8
   // XCDs; consecutive logical ranges (the blocks of one head) stay on one
   // XCD and share its L2 for the head's K and V.
@@ -69,7 +73,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_stream_kernel(Params p, Str
     float* part = nullptr;
     if (t0 != 0 || t1 != sp.ntb)
       part = sp.part + ((size_t)w * 2 + (first ? 0 : 1)) * (size_t)(BM * (D + 3));
-    fa_fwd_block<D, BN, NW, RB, S, PIPE, false, T>(p, head, qb, t0, t1, part, smem, vts);
+    fa_fwd_block<D, BN, NW, RB, S, PIPE, VT, false, T>(p, head, qb, t0, t1, part, smem, vts);
     g += t1 - t0;
     first = false;
     if (g < g_hi) {
