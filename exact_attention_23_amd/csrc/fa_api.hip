@@ -41,15 +41,17 @@ Variant make_variant(bool causal) {
 // can override them with -DFA_TILES_D32=... etc. to compare configurations.
 // All three read V^T straight from the V tiles (VT = 0); measured against the
 // transposed copy (same box, interleaved): 470 vs 480 us (yolo80b16), 2129
-// vs 2148 us (long16k). At d = 64 the smaller LDS footprint (48 KB with a
-// 3-stage ring) lets three 4-wave workgroups of one 32-row block per wave
-// share a CU (155 registers): 409 vs 417 us on seq2048, the same as two
-// row blocks per wave at two workgroups per CU, without its spills.
+// vs 2148 us (long16k). At d = 64 the smaller LDS footprint lets three
+// 4-wave workgroups of one 32-row block per wave share a CU (155
+// registers): 409 vs 417 us on seq2048 with a 3-stage ring (48 KB), 393 vs
+// 402 us with a 2-stage ring (32 KB). Measured and not kept: the pipelined
+// loop at d = 64 (408 vs 402) and d = 128 (2138 vs 2087), one row block per
+// wave at d = 32 (four workgroups per CU: 467 vs 461).
 #ifndef FA_TILES_D32
 #define FA_TILES_D32 32, 64, 4, 2, 4, true, 0
 #endif
 #ifndef FA_TILES_D64
-#define FA_TILES_D64 64, 64, 4, 1, 3, false, 0
+#define FA_TILES_D64 64, 64, 4, 1, 2, false, 0
 #endif
 #ifndef FA_TILES_D128
 #define FA_TILES_D128 128, 64, 8, 1, 4, false, 0
