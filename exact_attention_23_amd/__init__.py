@@ -288,7 +288,7 @@ def attention_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float,
     """Attention on FP8 (e4m3) q, k, v with per-tensor dequantisation factors.
 
     q: [B, H, Nq, d], k and v: [B, H, Nk, d], contiguous torch.float8_e4m3fn
-    GPU tensors, d = 64 or 128; element x of q means q_descale * x (likewise
+    GPU tensors, d = 32, 64 or 128; element x of q means q_descale * x (likewise
     k, v). Returns (out, lse): out [B, H, Nq, d] in out_dtype (torch.bfloat16
     by default, or torch.float16), lse [B, H, Nq] float32 (None when
     return_lse is False). scale=None means 1/sqrt(d).

@@ -95,18 +95,19 @@ __device__ __forceinline__ int lds_row_to_key(int r) {
 }
 
 // Byte offset of 16-byte chunk c of row r in an LDS tile with ROW_BYTES per
-// row (64, 128 or 256). Chunks are XOR-swizzled per row so that every read
+// row (32, 64, 128 or 256). Chunks are XOR-swizzled per row so that every read
 // pattern of the kernel touches 16 distinct 16-byte bank groups of a
 // 256-byte window per 16 lanes: one chunk of 16 consecutive rows (the MFMA
 // A operands) and 2 adjacent chunks of 4 consecutive rows starting at a
 // multiple of 4 (the transpose reads).
 template <int ROW_BYTES>
 __device__ __forceinline__ int lds_off(int r, int c) {
-  static_assert(ROW_BYTES == 64 || ROW_BYTES == 128 || ROW_BYTES == 256, "row size");
+  static_assert(ROW_BYTES == 32 || ROW_BYTES == 64 || ROW_BYTES == 128 || ROW_BYTES == 256, "row size");
   int swz;
   if (ROW_BYTES == 256) swz = ((r & 7) << 1) | ((r >> 3) & 1);             // 1 row per window
   else if (ROW_BYTES == 128) swz = (((r >> 1) & 3) << 1) | ((r >> 3) & 1);  // 2 rows
-  else swz = (r >> 2) & 3;                                                  // 4 rows
+  else if (ROW_BYTES == 64) swz = (r >> 2) & 3;                             // 4 rows
+  else swz = (r >> 3) & 1;  // 8 rows of 2 chunks: rows r and r+8 swap chunks
   return r * ROW_BYTES + 16 * (c ^ swz);
 }
 

@@ -15,15 +15,15 @@ namespace {
 
 typedef void (*Fp8Fn)(fa::Fp8Params);
 
-// 4 waves of 32 query rows, 64-key tiles, a 4-stage ring (40 KB of LDS at
-// d = 64, 80 KB at d = 128).
+// 4 waves of 32 query rows, 64-key tiles, a 4-stage ring (20 KB of LDS at
+// d = 32, 40 KB at d = 64, 80 KB at d = 128).
 template <int D, typename TO>
 Fp8Fn pick_d(bool causal) {
   return causal ? fa::fa_fwd_fp8_kernel<D, 4, 4, true, TO> : fa::fa_fwd_fp8_kernel<D, 4, 4, false, TO>;
 }
 template <typename TO>
 Fp8Fn pick_fp8(int64_t d, bool causal) {
-  return d == 64 ? pick_d<64, TO>(causal) : pick_d<128, TO>(causal);
+  return d == 32 ? pick_d<32, TO>(causal) : (d == 64 ? pick_d<64, TO>(causal) : pick_d<128, TO>(causal));
 }
 constexpr int kRows = 128;  // query rows per workgroup
 constexpr int kThreads = 256;
@@ -39,7 +39,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   // ---- every check happens before the first HIP call
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FA_ERR_NULLPTR;
   if (out_dtype != FA_DTYPE_FP16 && out_dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (d != 32 && d != 64 && d != 128) return FA_ERR_HEADDIM;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
   const int64_t lim = (int64_t)1 << 31;
   const int64_t head_lim = (int64_t)1 << 29;

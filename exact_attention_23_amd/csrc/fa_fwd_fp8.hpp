@@ -25,6 +25,10 @@
 //   * V^T comes from ds_read_b64_tr_b8: lane x of a 16-lane group points at
 //     row k0 + x/2, bytes 8*(x%2) of a 16-byte column block and receives
 //     rows k0..k0+7 of column x, stored as one 8-byte run of V^T row x.
+//   * d = 32 fills half of the 64-deep Q K^T step: the lanes of the second
+//     half (h = 1) supply zeros for both operands, so their products add
+//     nothing. A 2 KB K (or V) tile is 128 chunks of 16 bytes, so the first
+//     half of the waves loads K and the second half V.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -68,17 +72,21 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_fp8_kernel(Fp8Params pp) {
   constexpr int BN = 64;                     // keys per tile (two 32-key units)
   constexpr int BM = 32 * NW;                // query rows per workgroup
   constexpr int NT = 64 * NW;
-  constexpr int KS = D / 64;                 // 64-deep k-steps of Q K^T
+  constexpr int KS = D >= 64 ? D / 64 : 1;   // 64-deep k-steps of Q K^T
+  constexpr bool HALF_K = D == 32;            // d = 32: lanes h = 1 supply zeros
   constexpr int NDT = D / 32;                // 32-wide d tiles of O
   constexpr int CPR = D / 16;                // 16-byte chunks per K/V row
   constexpr int TILE = BN * D;               // bytes of a K (or V) tile
-  constexpr int CPT = TILE / 16 / NT;        // HBM->LDS loads per thread per tensor
-  constexpr int LOADS = 2 * CPT;
+  // HBM->LDS loads per thread per tensor; d = 32: K by the first NW/2 waves,
+  // V by the others, one load each per tile
+  constexpr bool SPLIT = TILE / 16 < NT;
+  constexpr int CPT = SPLIT ? 1 : TILE / 16 / NT;
+  constexpr int LOADS = SPLIT ? 1 : 2 * CPT;
   constexpr int TBLK = (BN / 8) * (D / 16);  // 8-key x 16-column transpose blocks
   constexpr int TPW = TBLK / (4 * NW);       // transpose reads per wave per tile
   constexpr int PENDING = (S - 3) * LOADS;
-  static_assert(D == 64 || D == 128, "fp8 path: d = 64 or 128");
-  static_assert(CPT >= 1 && CPT * NT * 16 == TILE, "tile must split evenly over threads");
+  static_assert(D == 32 || D == 64 || D == 128, "fp8 path: d = 32, 64 or 128");
+  static_assert(SPLIT ? TILE / 16 * 2 == NT : CPT * NT * 16 == TILE, "tile must split evenly over threads");
   static_assert(TPW >= 1 && TPW * 4 * NW == TBLK, "V transpose must split evenly over waves");
   static_assert(S >= 3 && PENDING < 64, "stage count out of range");
 
@@ -109,12 +117,15 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_fp8_kernel(Fp8Params pp) {
   i32x8 qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
+    // d = 32: the second lane half's d range (32..63) is past the row; it
+    // reads the next row's bytes and is zeroed (q_and/q_xor masks below)
     u32x4 w0 = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, q_row * D + 64 * s + 32 * half, 0, 0);
     u32x4 w1 = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, q_row * D + 64 * s + 32 * half + 16, 0, 0);
+    const uint32_t keep = (HALF_K && half) ? 0u : 0xffffffffu;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      w0[e] = (w0[e] & p.q_and) ^ p.q_xor;
-      w1[e] = (w1[e] & p.q_and) ^ p.q_xor;
+      w0[e] = ((w0[e] & p.q_and) ^ p.q_xor) & keep;
+      w1[e] = ((w1[e] & p.q_and) ^ p.q_xor) & keep;
     }
     qf[s] = join(w0, w1);
   }
@@ -143,9 +154,10 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_fp8_kernel(Fp8Params pp) {
 
   // ---- HBM -> LDS (K rows permuted, V rows natural)
   uint32_t k_goff[CPT], v_goff[CPT];
+  const int lwave = SPLIT ? wave % (NW / 2) : wave;  // the wave's block within its tensor
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int sl = (wave * CPT + i) * 64 + lane;
+    const int sl = (lwave * CPT + i) * 64 + lane;
     const int r = sl / CPR;
     const int ch = (lds_off<D>(r, sl % CPR) - r * D) >> 4;
     const int kkey = (r & ~31) | lds_row_to_key(r & 31);
@@ -159,9 +171,11 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_fp8_kernel(Fp8Params pp) {
     const uint32_t gb = t < ntiles ? (uint32_t)(t * TILE) : kOutOfRange;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const uint32_t blk = (uint32_t)((wave * CPT + i) * 1024);
-      dma_to_lds(k_rsrc, __builtin_amdgcn_readfirstlane(lds_base + (2 * st) * TILE + blk), k_goff[i] + gb);
-      dma_to_lds(v_rsrc, __builtin_amdgcn_readfirstlane(lds_base + (2 * st + 1) * TILE + blk), v_goff[i] + gb);
+      const uint32_t blk = (uint32_t)((lwave * CPT + i) * 1024);
+      if (!SPLIT || wave < NW / 2)
+        dma_to_lds(k_rsrc, __builtin_amdgcn_readfirstlane(lds_base + (2 * st) * TILE + blk), k_goff[i] + gb);
+      if (!SPLIT || wave >= NW / 2)
+        dma_to_lds(v_rsrc, __builtin_amdgcn_readfirstlane(lds_base + (2 * st + 1) * TILE + blk), v_goff[i] + gb);
     }
   };
 
@@ -213,7 +227,9 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_fp8_kernel(Fp8Params pp) {
     for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const i32x8 a = join(*(const u32x4*)(ks + k_off[t][s]), *(const u32x4*)(ks + k_off2[t][s]));
+        // d = 32: the second lane half has no K bytes (its Q half is zero)
+        const i32x8 a = (HALF_K && half) ? i32x8{}
+                                         : join(*(const u32x4*)(ks + k_off[t][s]), *(const u32x4*)(ks + k_off2[t][s]));
         sacc[t] = mfma_fp8(a, qf[s], s == 0 ? f32x16{} : sacc[t]);
       }
     if (MASK) {

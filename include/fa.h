@@ -205,7 +205,7 @@ int fa_fwd_stream(const void* q, const void* k, const void* v, void* o, float* l
  *   o          [B, H, Nq, d] contiguous output in out_dtype (FA_DTYPE_FP16 or
  *              FA_DTYPE_BF16)
  *   lse, B, H, Nq, Nk, scale, causal, stream: as in fa_fwd
- *   d          64 or 128
+ *   d          32, 64 or 128 (d = 32 fills half of each 64-deep Q K^T step)
  * Computes the forward of the dequantised tensors: S = scale * q_descale *
  * k_descale * (Q K^T on the e4m3 values, fp32 accumulation), O = softmax(S) V.
  * The attention weights are rounded to e4m3 (after scaling so that the

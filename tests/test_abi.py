@@ -299,7 +299,7 @@ def fcall(**kw):
     (dict(q=None), _lib.FA_ERR_NULLPTR),
     (dict(o=None), _lib.FA_ERR_NULLPTR),
     (dict(out_dtype=2), _lib.FA_ERR_DTYPE),
-    (dict(d=32), _lib.FA_ERR_HEADDIM),
+    (dict(d=16), _lib.FA_ERR_HEADDIM),
     (dict(d=96), _lib.FA_ERR_HEADDIM),
     (dict(Nq=0), _lib.FA_ERR_SHAPE),
     (dict(causal=2), _lib.FA_ERR_CAUSAL),

@@ -115,6 +115,11 @@ SMALL = [
     (2, 2, 100, 700, 64, False),
     (1, 2, 700, 100, 128, True),
     (1, 1, 1, 513, 64, False),
+    # d = 32: half of each 64-deep Q K^T step, K and V loaded by separate waves
+    (1, 1, 1, 1, 32, False),
+    (2, 2, 63, 65, 32, True),
+    (1, 2, 300, 257, 32, False),
+    (1, 1, 700, 100, 32, True),
 ]
 
 
@@ -141,20 +146,20 @@ def test_fp8_large_logits():
     """q, k ~ N(0, 8^2): nearly one-hot rows."""
     require_gpu()
     note("fp8 large logits")
-    for d in (64, 128):
+    for d in (32, 64, 128):
         for causal in (False, True):
             full_compare(2, 2, 361, 361, d, causal, seed=d, out_dtype=torch.float16, sigma=8.0,
                          what=f"large logits d={d} causal={causal}")
 
 
-def test_fp8_rejects_d32_and_bad_descale():
+def test_fp8_rejects_d16_and_bad_descale():
     require_gpu()
     w = Workload("t", 1, 1, 64, 64, 64, "bf16", False, seed=1)
     q8, k8, v8, sq, sk, sv = make_inputs_fp8(w)
     q8, k8, v8 = (t.to(DEV) for t in (q8, k8, v8))
     with pytest.raises(fa.FaError) as e:
-        fa.attention_fp8(q8[..., :32].contiguous(), k8[..., :32].contiguous(),
-                         v8[..., :32].contiguous(), sq, sk, sv)
+        fa.attention_fp8(q8[..., :16].contiguous(), k8[..., :16].contiguous(),
+                         v8[..., :16].contiguous(), sq, sk, sv)
     assert e.value.status == fa._lib.FA_ERR_HEADDIM
     for bad in (0.0, -1.0, float("nan"), float("inf")):
         with pytest.raises(fa.FaError) as e:
@@ -169,7 +174,7 @@ def _sample_rows(N, rng, n=40):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("name", ["seq2048", "long16k", "tail361"])
+@pytest.mark.parametrize("name", ["yolo80b16", "seq2048", "long16k", "tail361"])
 def test_fp8_named_workload_full_size(name):
     """The named workloads with their inputs quantised to e4m3, at full size;
     sampled rows of a few heads."""

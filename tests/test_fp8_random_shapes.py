@@ -24,7 +24,7 @@ def _cases():
         out.append(dict(
             B=int(rng.integers(1, 4)), H=int(rng.integers(1, 5)),
             Nq=int(rng.integers(1, 701)), Nk=int(rng.integers(1, 701)),
-            d=int(rng.choice([64, 128])), causal=bool(rng.integers(0, 2)),
+            d=int(rng.choice([32, 64, 128])), causal=bool(rng.integers(0, 2)),
             out_dtype=str(rng.choice(["bf16", "fp16"])),
             scale=(None if rng.random() < 0.5 else float(rng.uniform(-1.0, 1.0))),
             sigma=float(rng.choice([1.0, 2.0])), seed=8000 + i))
