@@ -186,7 +186,6 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
   constexpr int PENDING = (S - AHEAD) * LOADS;
   static_assert(S >= AHEAD && PENDING < 64, "stage count out of range");
 
-
   int tid = threadIdx.x;
   // Opaque to the optimiser, so the address arithmetic below is redone in
   // each pass instead of being hoisted out of the caller's pass loop and
@@ -523,24 +522,23 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
     __syncthreads();
   };
 
-  // ---- the plain loop: one tile at a time. Q K^T of both units, mask, P
-  // and row sums, one acceptance test for the tile (raising the reference to
-  // the tile's maximum when it fails), then P V.
-  auto plain_tile = [&](auto mask_tag, int j) {
-    {
-      // k-step outer, unit inner: consecutive MFMAs feed different
-      // accumulators
-      const char* ks = smem[(j - t_lo) % S][0];
+  // ---- the steps of a tile: Q K^T of both units; mask, P and row sums with
+  // one acceptance test for the tile (raising the reference to the tile's
+  // maximum when it fails); P V.
+  auto qk_step = [&](int j) {
+    // k-step outer, unit inner: consecutive MFMAs feed different accumulators
+    const char* ks = smem[(j - t_lo) % S][0];
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const vec a = *(const vec*)(ks + k_roff[t][s]);
+      for (int t = 0; t < 2; ++t) {
+        const vec a = *(const vec*)(ks + k_roff[t][s]);
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            sacc[t][rb] = M::run(a, qf[rb][s], s == 0 ? f32x16{} : sacc[t][rb]);
-        }
-    }
+        for (int rb = 0; rb < RB; ++rb)
+          sacc[t][rb] = M::run(a, qf[rb][s], s == 0 ? f32x16{} : sacc[t][rb]);
+      }
+  };
+  auto softmax_step = [&](auto mask_tag, int j) {
     if (decltype(mask_tag)::value) {
       mask_unit(j, 0, sacc[0]);
       mask_unit(j, 1, sacc[1]);
@@ -564,12 +562,21 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
       l_run[rb] += psum[0][rb] + psum[1][rb];
       if constexpr (M::kLse32) l32_run[rb] += ps32[0][rb] + ps32[1][rb];
     }
+  };
+  auto pv_step = [&](int j) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       vec vf[2][NDT];
       load_v(j, t, vf);
       pv(vf, pf[t]);
     }
+  };
+
+  // ---- the plain loop: one tile at a time, all waves in step.
+  auto plain_tile = [&](auto mask_tag, int j) {
+    qk_step(j);
+    softmax_step(mask_tag, j);
+    pv_step(j);
     tile_end();
   };
 
