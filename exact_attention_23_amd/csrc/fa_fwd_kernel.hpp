@@ -282,8 +282,9 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
   // Offsets of tiles past the end are pushed beyond every buffer's range:
   // those loads only write zeros to LDS and touch no memory.
   constexpr uint32_t kOutOfRange = 0x40000000u;
-  auto issue = [&](int t) {
-    const int st = (t - t_lo) % S;
+  // Tile t goes to ring stage st = (t - t_lo) % S; the callers pass st, a
+  // constant where the loop is unrolled over the ring.
+  auto issue = [&](int t, int st) {
     const uint32_t kbase = t < t_hi ? (uint32_t)(t * BN * krs) : kOutOfRange;
     const uint32_t vbase = t < t_hi ? (uint32_t)(t * BN * vrs) : kOutOfRange;
 #pragma unroll
@@ -329,10 +330,10 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
       for (int s2 = 0; s2 < 2; ++s2)
         v_roff[dt][t][s2] = lds_off<2 * BN>(32 * dt + r32, 4 * t + 2 * half + s2);
 
-  // V tile j (as loaded) -> V^T buffer j % 2 (VT = 1 only)
-  auto transpose_v = [&](int j) {
+  // V tile j (as loaded, in stage st) -> V^T buffer j % 2 (VT = 1 only)
+  auto transpose_v = [&](int j, int st) {
     if constexpr (VT != 0) {
-      const char* vsrc = smem[(j - t_lo) % S][1];
+      const char* vsrc = smem[st][1];
       char* vdst = vts + ((j - t_lo) & 1) * TILE_BYTES;
       i16x4 blk[TPW];
 #pragma unroll
@@ -381,12 +382,12 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
   // LDS operands of one unit: K rows of subtile t of tile j (A operands of
   // S^T = K Q^T, one per k-step) and V^T of subtile t of tile j (A operands
   // of O^T += V^T P^T, per 16-key half s2 and 32-wide d tile).
-  auto load_k = [&](int j, int t, vec (&kf)[KS]) {
-    const char* ks = smem[(j - t_lo) % S][0];
+  auto load_k = [&](int st, int t, vec (&kf)[KS]) {
+    const char* ks = smem[st][0];
 #pragma unroll
     for (int s = 0; s < KS; ++s) kf[s] = *(const vec*)(ks + k_roff[t][s]);
   };
-  auto load_v = [&](int j, int t, vec (&vf)[2][NDT]) {
+  auto load_v = [&](int j, int st, int t, vec (&vf)[2][NDT]) {
     if constexpr (VT != 0) {
       const char* vs = vts + ((j - t_lo) & 1) * TILE_BYTES;
 #pragma unroll
@@ -394,7 +395,7 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) vf[s2][dt] = *(const vec*)(vs + v_roff[dt][t][s2]);
     } else {
-      const char* vs = smem[(j - t_lo) % S][1];
+      const char* vs = smem[st][1];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -513,9 +514,9 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
   // has landed). End of tile j: wait until tile j+2 has landed (this wave's
   // own loads) and meet the other waves at the barrier. Past the last tile
   // the stages hold zeros from out-of-range loads.
-  auto tile_start = [&](int j) {
-    issue(j + S - 1);
-    transpose_v(j + 1);
+  auto tile_start = [&](int j, int st) {
+    issue(j + S - 1, (st + S - 1) % S);
+    transpose_v(j + 1, (st + 1) % S);
   };
   auto tile_end = [&]() {
     wait_vmcnt<PENDING>();
@@ -525,9 +526,9 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
   // ---- the steps of a tile: Q K^T of both units; mask, P and row sums with
   // one acceptance test for the tile (raising the reference to the tile's
   // maximum when it fails); P V.
-  auto qk_step = [&](int j) {
+  auto qk_step = [&](int st) {
     // k-step outer, unit inner: consecutive MFMAs feed different accumulators
-    const char* ks = smem[(j - t_lo) % S][0];
+    const char* ks = smem[st][0];
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
@@ -563,20 +564,20 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
       if constexpr (M::kLse32) l32_run[rb] += ps32[0][rb] + ps32[1][rb];
     }
   };
-  auto pv_step = [&](int j) {
+  auto pv_step = [&](int j, int st) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       vec vf[2][NDT];
-      load_v(j, t, vf);
+      load_v(j, st, t, vf);
       pv(vf, pf[t]);
     }
   };
 
   // ---- the plain loop: one tile at a time, all waves in step.
-  auto plain_tile = [&](auto mask_tag, int j) {
-    qk_step(j);
+  auto plain_tile = [&](auto mask_tag, int j, int st) {
+    qk_step(st);
     softmax_step(mask_tag, j);
-    pv_step(j);
+    pv_step(j, st);
     tile_end();
   };
 
@@ -590,7 +591,8 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
   constexpr int NMF = RB * KS;  // Q K^T MFMAs of a unit
   constexpr int NPR = RB * 8;   // P pairs of a unit
   auto piped_unit = [&](auto mask_tag, int j, int t, f32x16 (&sr)[RB], vec (&pr)[RB][2],
-                        float (&ps)[RB], float (&p32)[RB], const vec (&kf)[KS], f32x16 (&sn)[RB]) {
+                        float (&ps)[RB], float (&p32)[RB], const vec (&kf)[KS], f32x16 (&sn)[RB],
+                        int st) {
     if (decltype(mask_tag)::value) mask_unit(j, t, sr);
     float negm[RB], lsum[RB], lrnd[RB];
     u32x4 w[RB][2];
@@ -631,7 +633,7 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
       p32[rb] = lsum[rb];
     }
     vec vf[2][NDT];
-    load_v(j, t, vf);
+    load_v(j, st, t, vf);
     if ((strict || (j == t_lo && t == 0)) && __any(!unit_ok(ps))) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -646,27 +648,27 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
     }
     pv(vf, pr);
   };
-  auto piped_tile = [&](auto mask_tag, int j) {
+  auto piped_tile = [&](auto mask_tag, int j, int st) {
     {  // unit (j, 0), with Q K^T of unit (j, 1)
       vec kf[KS];
-      load_k(j, 1, kf);
-      piped_unit(mask_tag, j, 0, sacc[0], pf[0], psum[0], ps32[0], kf, sacc[1]);
+      load_k(st, 1, kf);
+      piped_unit(mask_tag, j, 0, sacc[0], pf[0], psum[0], ps32[0], kf, sacc[1], st);
     }
     {  // unit (j, 1), with Q K^T of unit (j+1, 0)
       vec kf[KS];
-      load_k(j + 1, 0, kf);
-      piped_unit(mask_tag, j, 1, sacc[1], pf[1], psum[1], ps32[1], kf, sacc[0]);
+      load_k((st + 1) % S, 0, kf);
+      piped_unit(mask_tag, j, 1, sacc[1], pf[1], psum[1], ps32[1], kf, sacc[0], st);
     }
     tile_end();
   };
 
   // ---- prologue: tiles t_lo..t_lo+S-2 requested, V^T of tile t_lo written.
 #pragma unroll
-  for (int t = 0; t < S - 1; ++t) issue(t_lo + t);
+  for (int t = 0; t < S - 1; ++t) issue(t_lo + t, t);
   wait_vmcnt<PENDING>();
   __syncthreads();
   if constexpr (VT != 0) {
-    transpose_v(t_lo);
+    transpose_v(t_lo, 0);
     __syncthreads();
   }
 
@@ -679,38 +681,61 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
   const auto masked = std::integral_constant<bool, true>{};
   const int j_free = first_masked < t_hi ? first_masked : t_hi;
   int j = t_lo;
+  auto stage = [&](int jj) { return (jj - t_lo) % S; };
+  // The unmasked tiles run S at a time from t_lo, so that the ring stage of
+  // each is a constant and every LDS operand address is a per-lane base plus
+  // an immediate offset; the rest (fewer than S unmasked tiles, and the
+  // masked ones) take the stage at run time. At d = 128 the per-lane bases
+  // of all K and V^T reads (24 registers) do not fit beside the operands,
+  // and every tile takes the stage at run time.
+  constexpr bool kRingUnroll = D <= 64;
+  auto ring_steps = [&](auto body) {
+    if constexpr (kRingUnroll)
+      for (; j + S <= j_free; j += S)
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        (body(j + I, I), ...);
+      }(std::make_integer_sequence<int, S>{});
+  };
   if constexpr (PIPE) {
     // Scores of the first unit before the loop; its test raises the
     // reference from -inf.
     {
       vec kf[KS];
-      load_k(t_lo, 0, kf);
+      load_k(0, 0, kf);
       qk(kf, sacc[0]);
     }
+    ring_steps([&](int jj, int st) {
+      tile_start(jj, st);
+      piped_tile(unmasked, jj, st);
+    });
     for (; j < j_free; ++j) {
-      tile_start(j);
-      piped_tile(unmasked, j);
+      tile_start(j, stage(j));
+      piped_tile(unmasked, j, stage(j));
     }
     for (; j < t_hi && !beyond_rows(j); ++j) {
-      tile_start(j);
-      piped_tile(masked, j);
+      tile_start(j, stage(j));
+      piped_tile(masked, j, stage(j));
     }
   }
   if constexpr (!PIPE) {
+    ring_steps([&](int jj, int st) {
+      tile_start(jj, st);
+      plain_tile(unmasked, jj, st);
+    });
     for (; j < j_free; ++j) {
-      tile_start(j);
-      plain_tile(unmasked, j);
+      tile_start(j, stage(j));
+      plain_tile(unmasked, j, stage(j));
     }
     for (; j < t_hi && !beyond_rows(j); ++j) {
-      tile_start(j);
-      plain_tile(masked, j);
+      tile_start(j, stage(j));
+      plain_tile(masked, j, stage(j));
     }
   }
 
   // Causal tiles past this wave's rows: only its share of the loads,
   // transposes and barriers.
   for (; j < t_hi; ++j) {
-    tile_start(j);
+    tile_start(j, stage(j));
     tile_end();
   }
 
