@@ -30,11 +30,15 @@
 //   * Those registers, rounded in pairs, are directly the A operand (P^T,
 //     dS^T: row = key, k = 8 queries) of dV += P^T dO and dK += dS^T Q, with
 //     the queries of a k-step taken in that register order. The B operands
-//     (dO and Q with the queries along k) come from transposed copies, Q^T and
-//     dO^T, written once per workgroup per tile, one tile ahead, with
-//     ds_read_b64_tr_b16; inside each group of 16 queries the copies store the
-//     queries in the order 0-3, 8-11, 4-7, 12-15 (bits 2 and 3 swapped), so a
-//     lane's eight queries are one 16-byte run.
+//     (dO and Q with the queries along k) come from ds_read_b64_tr_b16
+//     transpose reads. At d <= 64 they are read straight from the staged
+//     tiles (two transpose reads per operand, each handing a lane 4
+//     consecutive queries of its d column). At d = 128, where the direct
+//     reads' addresses do not fit in the registers beside the operands,
+//     they come from transposed copies, Q^T and dO^T, written once per
+//     workgroup per tile, one tile ahead; inside each group of 16 queries the
+//     copies store the queries in the order 0-3, 8-11, 4-7, 12-15 (bits 2
+//     and 3 swapped), so a lane's eight queries are one 16-byte run.
 //   * LSE and D of the 16 queries of a lane are four 16-byte LDS reads each
 //     (the lanes of a half read the same address).
 //   * Q, dO and the workspace records go HBM -> LDS by buffer_load ... lds
@@ -42,8 +46,12 @@
 // The dQ kernel is the forward's structure with a different per-unit body:
 // S^T = K Q^T and dP^T = V dO^T (K and V rows as A operands from LDS in the
 // permuted key order, Q and dO of the wave's rows as B operands in VGPRs),
-// then dQ^T += K^T dS^T with K^T transposed once per tile like the forward's
-// V^T, and dS^T straight from the accumulator registers.
+// then dQ^T += K^T dS^T with dS^T straight from the accumulator registers and
+// the K^T operand, like the B operands above, read straight from the K tile
+// at d <= 64 and from a copy transposed once per tile at d = 128. Tiles that
+// are read directly use the forward's swizzle (tile_off), under which both
+// the operand reads and the transpose reads are free of bank conflicts; the
+// copy path keeps lds_off, which suits its transposes.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -142,8 +150,7 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p) {
 #endif
 
 // Waves per SIMD the backward kernels are compiled for (register budget).
-// d = 32 dQ: 130 registers would allow three waves, capped at 128 (3 spilled)
-// four, 2% faster. (d = 64 dK/dV capped at three waves ran 2-3% faster but
+// d = 32 dQ: capped at four waves (128 registers; it takes about 100). (d = 64 dK/dV capped at three waves ran 2-3% faster but
 // its 11 spilled registers added 40% to its HBM traffic; it is not capped.)
 constexpr int bwd_dkdv_min_waves(int) { return 1; }
 constexpr int bwd_dq_min_waves(int d) { return d == 32 ? 4 : 1; }
@@ -163,20 +170,25 @@ __global__ __launch_bounds__(NW * 64, bwd_dkdv_min_waves(D)) void fa_bwd_dkdv_ke
   constexpr int AUXB = BM * 8;               // bytes of a tile's LSE and D
   constexpr int AUX_LANES = AUXB / 16 / NW;  // lanes per wave loading them
   constexpr int LOADS = CPT + 1;             // loads per wave per tile
-  constexpr int TBLK = (BM / 4) * (D / 16);  // 4-row x 16-column blocks per tensor
-  constexpr int TPW = 2 * TBLK / (4 * NW);   // transpose reads per wave per tile
-  constexpr int PENDING = (S - 3) * LOADS;
+  constexpr bool DIRECT = D <= 64;           // B operands straight from the staged tiles
+  constexpr int TBLK = (BM / 4) * (D / 16);  // copy path: 4-row x 16-column blocks per tensor
+  constexpr int TPW = 2 * TBLK / (4 * NW);   // copy path: transpose reads per wave per tile
+  // Loads left in flight at the end of step j: tile j+1 must have landed
+  // (the copy path transposes tile j+1 during step j, so tile j+2 there).
+  constexpr int PENDING = (S - (DIRECT ? 2 : 3)) * LOADS;
   static_assert(CPT >= 1 && CPT * NT * 16 == 2 * TILE, "Q and dO tiles must split over threads");
   static_assert(TILE % 1024 == 0, "a 1 KB load block must not straddle Q and dO");
   static_assert(AUX_LANES >= 1 && AUX_LANES * 16 * NW == AUXB, "records must split over waves");
-  static_assert(TPW >= 1 && TPW * 4 * NW == 2 * TBLK, "transposes must split over waves");
-  static_assert(TBLK % 4 == 0, "a wave's transpose groups must stay in one tensor");
-  static_assert(S >= 3 && PENDING < 64, "stage count out of range");
+  static_assert(DIRECT || (TPW >= 1 && TPW * 4 * NW == 2 * TBLK), "transposes must split over waves");
+  static_assert(DIRECT || TBLK % 4 == 0, "a wave's transpose groups must stay in one tensor");
+  static_assert(PENDING >= 0 && PENDING < 64, "stage count out of range");
+  auto toff = [](int r, int c) { return DIRECT ? tile_off<2 * D>(r, c) : lds_off<2 * D>(r, c); };
 
-  // Staged tiles ([stage][Q, dO], rows = queries), their transposes
-  // ([parity][Q^T, dO^T], rows = d columns of 32 queries) and the records.
+  // Staged tiles ([stage][Q, dO], rows = queries), the copy path's
+  // transposes ([parity][Q^T, dO^T], rows = d columns of 32 queries) and the
+  // records.
   __shared__ __attribute__((aligned(1024))) char ring[S][2][TILE];
-  __shared__ __attribute__((aligned(1024))) char trb[2][2][TILE];
+  __shared__ __attribute__((aligned(1024))) char trb[DIRECT ? 1 : 2][2][DIRECT ? 16 : TILE];
   __shared__ __attribute__((aligned(16))) float auxs[S][2 * BM];
   // At d = 128 the wave's K rows live in LDS instead of VGPRs (the registers
   // are full there); each wave reads back only its own 32 rows.
@@ -259,7 +271,7 @@ __global__ __launch_bounds__(NW * 64, bwd_dkdv_min_waves(D)) void fa_bwd_dkdv_ke
     const int tensor = (blk * 1024) / TILE;
     const int sl = (blk * 1024 - tensor * TILE) / 16 + lane;
     const int r = sl / CPR;
-    const int ch = (lds_off<2 * D>(r, sl % CPR) - r * (2 * D)) >> 4;
+    const int ch = (toff(r, sl % CPR) - r * (2 * D)) >> 4;
     goff[i] = r * (2 * D) + 16 * ch;
   }
   const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&ring[0][0][0];
@@ -282,46 +294,68 @@ __global__ __launch_bounds__(NW * 64, bwd_dkdv_min_waves(D)) void fa_bwd_dkdv_ke
                  ab + wave * (AUX_LANES * 16) + 16 * lane);
   };
 
-  // ---- transposes of a staged tile into Q^T / dO^T. Transpose read i of
-  // this wave covers, in 16-lane group G, rows q0..q0+3 and columns
+  // ---- copy path: transposes of a staged tile into Q^T / dO^T. Transpose
+  // read i of this wave covers, in 16-lane group G, rows q0..q0+3 and columns
   // d0..d0+15 of one tensor; lane x points at row q0 + x/4, columns
   // d0 + 4(x%4) .. +3, receives rows q0..q0+3 of column d0 + x and stores
   // them as one 8-byte run of row d0 + x of the copy, at the position of q0
   // in the bit-2/3-swapped query order.
-  int tr_src[TPW], tr_dst[TPW];
+  int tr_src[DIRECT ? 1 : TPW], tr_dst[DIRECT ? 1 : TPW];
+  if constexpr (!DIRECT) {
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int G = (wave * TPW + i) * 4 + (lane >> 4);
-    const int tensor = G / TBLK;
-    const int g = G - tensor * TBLK;
-    const int q0 = 4 * (g % (BM / 4));
-    const int d0 = 16 * (g / (BM / 4));
-    const int x = lane & 15;
-    const int col = d0 + 4 * (x & 3);
-    tr_src[i] = tensor * TILE + lds_off<2 * D>(q0 + (x >> 2), col >> 3) + 2 * (col & 7);
-    const int pos = (q0 & ~15) | (((q0 >> 3) & 1) << 2) | (((q0 >> 2) & 1) << 3);
-    tr_dst[i] = tensor * TILE + lds_off<2 * BM>(d0 + x, pos >> 3) + 2 * (pos & 7);
+    for (int i = 0; i < TPW; ++i) {
+      const int G = (wave * TPW + i) * 4 + (lane >> 4);
+      const int tensor = G / TBLK;
+      const int g = G - tensor * TBLK;
+      const int q0 = 4 * (g % (BM / 4));
+      const int d0 = 16 * (g / (BM / 4));
+      const int x = lane & 15;
+      const int col = d0 + 4 * (x & 3);
+      tr_src[i] = tensor * TILE + lds_off<2 * D>(q0 + (x >> 2), col >> 3) + 2 * (col & 7);
+      const int pos = (q0 & ~15) | (((q0 >> 3) & 1) << 2) | (((q0 >> 2) & 1) << 3);
+      tr_dst[i] = tensor * TILE + lds_off<2 * BM>(d0 + x, pos >> 3) + 2 * (pos & 7);
+    }
   }
   auto transpose = [&](int j) {
-    const char* src = &ring[j % S][0][0];
-    char* dst = &trb[j & 1][0][0];
-    i16x4 blk[TPW];
+    if constexpr (!DIRECT) {
+      const char* src = &ring[j % S][0][0];
+      char* dst = &trb[j & 1][0][0];
+      i16x4 blk[TPW];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i)
-      blk[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + tr_src[i]));
+      for (int i = 0; i < TPW; ++i)
+        blk[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + tr_src[i]));
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) *(i16x4*)(dst + tr_dst[i]) = blk[i];
+      for (int i = 0; i < TPW; ++i) *(i16x4*)(dst + tr_dst[i]) = blk[i];
+    }
   };
 
   // LDS read offsets that do not depend on the tile.
   int a_off[KS];  // Q / dO rows as A operands: row r32, chunk 2s + half
 #pragma unroll
-  for (int s = 0; s < KS; ++s) a_off[s] = lds_off<2 * D>(r32, 2 * s + half);
-  int b_off[NDT][2];  // Q^T / dO^T as B operands: row 32dt + r32, queries 16c2 + 8half ..
+  for (int s = 0; s < KS; ++s) a_off[s] = toff(r32, 2 * s + half);
+  int b_off[NDT][2];  // copy path: Q^T / dO^T rows 32dt + r32, queries 16c2 + 8half ..
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) b_off[dt][c2] = lds_off<2 * BM>(32 * dt + r32, 2 * c2 + half);
+  // Direct path: Q^T / dO^T B operand of d tile dt for k-step c2 (queries 16c2 + 4half +
+  // 0..3, then 8 on: the order of the P^T / dS^T registers) straight from
+  // the staged tile: two transpose reads, lane x of a 16-lane group pointing
+  // at query 16c2 + 4half + x/4 (then + 8), columns d0 + 4(x%4) .. +3 with
+  // d0 = 32dt + 16((lane/16)%2), and receiving 4 queries of column d0 + x.
+  const int trx = lane & 15;
+  const int tr_row = 4 * half + (trx >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (trx & 3);
+  auto b_direct = [&](const char* src, int c2, int dt) -> vec {
+    const int row = tr_row + 16 * c2;
+    const int col = tr_col + 32 * dt;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(src + tile_off<2 * D>(row, col >> 3) + 2 * (col & 7)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(src + tile_off<2 * D>(row + 8, col >> 3) + 2 * (col & 7)));
+    const u32x2 wl = __builtin_bit_cast(u32x2, lo), wh = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(vec, u32x4{wl[0], wl[1], wh[0], wh[1]});
+  };
 
   // ---- one query tile
   auto tile = [&](auto mask_tag, int j) {
@@ -332,8 +366,8 @@ __global__ __launch_bounds__(NW * 64, bwd_dkdv_min_waves(D)) void fa_bwd_dkdv_ke
     const char* qs = &ring[j % S][0][0];
     const char* dos = &ring[j % S][1][0];
     const float* ax = auxs[j % S];
-    const char* qt = &trb[j & 1][0][0];
-    const char* dot = &trb[j & 1][1][0];
+    const char* qt = &trb[DIRECT ? 0 : (j & 1)][0][0];
+    const char* dot = &trb[DIRECT ? 0 : (j & 1)][1][0];
     f32x16 sa, dpa;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -386,26 +420,29 @@ __global__ __launch_bounds__(NW * 64, bwd_dkdv_min_waves(D)) void fa_bwd_dkdv_ke
     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const vec bo = *(const vec*)(dot + b_off[dt][c2]);
-        const vec bq = *(const vec*)(qt + b_off[dt][c2]);
+        const vec bo = DIRECT ? b_direct(dos, c2, dt) : *(const vec*)(dot + b_off[dt][c2]);
+        const vec bq = DIRECT ? b_direct(qs, c2, dt) : *(const vec*)(qt + b_off[dt][c2]);
         dv[dt] = M::run(pa[c2], bo, dv[dt]);
         dk[dt] = M::run(da[c2], bq, dk[dt]);
       }
   };
 
   if (ntiles > 0) {
-    // prologue: tiles 0..S-2 requested; tiles 0 and 1 landed; tile 0 transposed
+    // prologue: tiles 0..S-2 requested; tile 0 landed (copy path: tiles 0
+    // and 1, and tile 0 transposed)
 #pragma unroll
     for (int t = 0; t < S - 1; ++t) issue(t);
     wait_vmcnt<PENDING>();
     __syncthreads();
-    transpose(0);
-    __syncthreads();
+    if constexpr (!DIRECT) {
+      transpose(0);
+      __syncthreads();
+    }
     const auto unmasked = std::integral_constant<bool, false>{};
     const auto masked = std::integral_constant<bool, true>{};
-    // Step j: request tile j+S-1 into the stage of tile j-1, transpose tile
-    // j+1, compute tile j; then wait until tile j+2 has landed and meet at
-    // the barrier.
+    // Step j: request tile j+S-1 into the stage of tile j-1, (copy path)
+    // transpose tile j+1, compute tile j; then wait until the next tile to
+    // read has landed and meet at the barrier.
     int j = 0;
     for (; j < first_free; ++j) {
       issue(j + S - 1);
@@ -457,17 +494,22 @@ __global__ __launch_bounds__(NW * 64, bwd_dq_min_waves(D)) void fa_bwd_dq_kernel
   constexpr int CPT = CHUNKS / NT;
   constexpr int TILE = BN * D * 2;
   constexpr int LOADS = 2 * CPT;
+  constexpr bool DIRECT = D <= 64;  // K^T operand straight from the K tile
   constexpr int TBLK = (BN / 4) * (D / 16);
   constexpr int TPW = TBLK / (4 * NW);
-  constexpr int PENDING = (S - 3) * LOADS;
+  // Loads left in flight at the end of step j: tile j+1 must have landed
+  // (the copy path transposes tile j+1 during step j, so tile j+2 there).
+  constexpr int PENDING = (S - (DIRECT ? 2 : 3)) * LOADS;
   static_assert(CPT >= 1 && CPT * NT == CHUNKS, "tile must split evenly over threads");
-  static_assert(TPW >= 1 && TPW * 4 * NW == TBLK, "K transpose must split evenly over waves");
-  static_assert(S >= 3 && PENDING < 64, "stage count out of range");
+  static_assert(DIRECT || (TPW >= 1 && TPW * 4 * NW == TBLK), "K transpose must split evenly over waves");
+  static_assert(PENDING >= 0 && PENDING < 64, "stage count out of range");
+  auto toff = [](int r, int c) { return DIRECT ? tile_off<2 * D>(r, c) : lds_off<2 * D>(r, c); };
 
   // K and V tiles as loaded ([stage][K, V], rows = keys in the permuted
-  // order) and K^T (rows = d, keys in natural order), double-buffered.
+  // order) and, on the copy path, K^T (rows = d, keys in natural order),
+  // double-buffered.
   __shared__ __attribute__((aligned(1024))) char smem[S][2][TILE];
-  __shared__ __attribute__((aligned(1024))) char kts[2][TILE];
+  __shared__ __attribute__((aligned(1024))) char kts[DIRECT ? 1 : 2][DIRECT ? 16 : TILE];
 
   int head, qb;
   bwd_work_item<CAUSAL>(p, blockIdx.x, head, qb);
@@ -534,7 +576,7 @@ __global__ __launch_bounds__(NW * 64, bwd_dq_min_waves(D)) void fa_bwd_dq_kernel
   for (int i = 0; i < CPT; ++i) {
     const int sl = (wave * CPT + i) * 64 + lane;
     const int r = sl / CPR;
-    const int ch = (lds_off<2 * D>(r, sl % CPR) - r * (2 * D)) >> 4;
+    const int ch = (toff(r, sl % CPR) - r * (2 * D)) >> 4;
     const int kkey = (r & ~31) | lds_row_to_key(r & 31);
     goff[i] = kkey * (2 * D) + 16 * ch;
   }
@@ -551,50 +593,75 @@ __global__ __launch_bounds__(NW * 64, bwd_dq_min_waves(D)) void fa_bwd_dq_kernel
     }
   };
 
-  // ---- K tile -> K^T. A 4-aligned run of LDS rows holds 4 consecutive keys
-  // (from key0 on), which the transpose read hands to a lane as one 8-byte
-  // run of its d column.
-  int tr_src[TPW], tr_dst[TPW];
+  // ---- copy path: K tile -> K^T. A 4-aligned run of LDS rows holds 4
+  // consecutive keys (from key0 on), which the transpose read hands to a
+  // lane as one 8-byte run of its d column.
+  int tr_src[DIRECT ? 1 : TPW], tr_dst[DIRECT ? 1 : TPW];
+  if constexpr (!DIRECT) {
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int G = (wave * TPW + i) * 4 + (lane >> 4);
-    const int r0 = 4 * (G % (BN / 4));
-    const int d0 = 16 * (G / (BN / 4));
-    const int x = lane & 15;
-    const int col = d0 + 4 * (x & 3);
-    tr_src[i] = lds_off<2 * D>(r0 + (x >> 2), col >> 3) + 2 * (col & 7);
-    const int key0 = (r0 & ~31) | lds_row_to_key(r0 & 31);
-    tr_dst[i] = lds_off<2 * BN>(d0 + x, key0 >> 3) + 2 * (key0 & 7);
+    for (int i = 0; i < TPW; ++i) {
+      const int G = (wave * TPW + i) * 4 + (lane >> 4);
+      const int r0 = 4 * (G % (BN / 4));
+      const int d0 = 16 * (G / (BN / 4));
+      const int x = lane & 15;
+      const int col = d0 + 4 * (x & 3);
+      tr_src[i] = lds_off<2 * D>(r0 + (x >> 2), col >> 3) + 2 * (col & 7);
+      const int key0 = (r0 & ~31) | lds_row_to_key(r0 & 31);
+      tr_dst[i] = lds_off<2 * BN>(d0 + x, key0 >> 3) + 2 * (key0 & 7);
+    }
   }
   auto transpose_k = [&](int j) {
-    const char* src = smem[j % S][0];
-    char* dst = kts[j & 1];
-    i16x4 blk[TPW];
+    if constexpr (!DIRECT) {
+      const char* src = smem[j % S][0];
+      char* dst = kts[j & 1];
+      i16x4 blk[TPW];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i)
-      blk[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + tr_src[i]));
+      for (int i = 0; i < TPW; ++i)
+        blk[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + tr_src[i]));
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) *(i16x4*)(dst + tr_dst[i]) = blk[i];
+      for (int i = 0; i < TPW; ++i) *(i16x4*)(dst + tr_dst[i]) = blk[i];
+    }
   };
 
   int a_off[2][KS];  // K / V rows of unit t: row 32t + r32, chunk 2s + half
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) a_off[t][s] = lds_off<2 * D>(32 * t + r32, 2 * s + half);
-  int kt_off[NDT][2][2];  // K^T rows 32dt + r32, keys 32t + 16half + 8s2 .. +7
+    for (int s = 0; s < KS; ++s) a_off[t][s] = toff(32 * t + r32, 2 * s + half);
+  int kt_off[NDT][2][2];  // copy path: K^T rows 32dt + r32, keys 32t + 16half + 8s2 .. +7
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) kt_off[dt][t][s2] = lds_off<2 * BN>(32 * dt + r32, 4 * t + 2 * half + s2);
+  // Direct path: K^T A operand of d tile dt for keys 32t + 16half + 8s2 .. +7 (natural
+  // order, the order of the dS^T registers) straight from the K tile. LDS
+  // row 16s2 + 4half + 0..3 (+ 32t) holds keys 16half + 8s2 + 0..3 and the
+  // rows 8 on hold the next 4 (the permuted order keeps 4-aligned runs of
+  // rows consecutive): two transpose reads, lane x of a 16-lane group
+  // pointing at row 16s2 + 4half + x/4 (then + 8), columns d0 + 4(x%4) ..
+  // +3 with d0 = 32dt + 16((lane/16)%2), and receiving 4 keys of column
+  // d0 + x.
+  const int trx = lane & 15;
+  const int tr_row = 4 * half + (trx >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (trx & 3);
+  auto kt_direct = [&](const char* ks, int t, int s2, int dt) -> vec {
+    const int row = tr_row + 32 * t + 16 * s2;
+    const int col = tr_col + 32 * dt;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(ks + tile_off<2 * D>(row, col >> 3) + 2 * (col & 7)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(ks + tile_off<2 * D>(row + 8, col >> 3) + 2 * (col & 7)));
+    const u32x2 wl = __builtin_bit_cast(u32x2, lo), wh = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(vec, u32x4{wl[0], wl[1], wh[0], wh[1]});
+  };
 
   auto unit = [&](auto mask_tag, int j, int t) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const char* ks = smem[j % S][0];
     const char* vs = smem[j % S][1];
-    const char* kt = kts[j & 1];
+    const char* kt = kts[DIRECT ? 0 : (j & 1)];
     f32x16 sa, dpa;
 #pragma unroll
     for (int s = 0; s < KS; ++s) sa = M::run(*(const vec*)(ks + a_off[t][s]), qf[s], s == 0 ? f32x16{} : sa);
@@ -625,16 +692,20 @@ __global__ __launch_bounds__(NW * 64, bwd_dq_min_waves(D)) void fa_bwd_dq_kernel
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) dq[dt] = M::run(*(const vec*)(kt + kt_off[dt][t][s2]), b[s2], dq[dt]);
+      for (int dt = 0; dt < NDT; ++dt)
+        dq[dt] = M::run(DIRECT ? kt_direct(ks, t, s2, dt) : *(const vec*)(kt + kt_off[dt][t][s2]), b[s2], dq[dt]);
   };
 
-  // prologue: tiles 0..S-2 requested, K^T of tile 0 written
+  // prologue: tiles 0..S-2 requested, tile 0 landed (copy path: tiles 0
+  // and 1, and K^T of tile 0 written)
 #pragma unroll
   for (int t = 0; t < S - 1; ++t) issue(t);
   wait_vmcnt<PENDING>();
   __syncthreads();
-  transpose_k(0);
-  __syncthreads();
+  if constexpr (!DIRECT) {
+    transpose_k(0);
+    __syncthreads();
+  }
   const auto unmasked = std::integral_constant<bool, false>{};
   const auto masked = std::integral_constant<bool, true>{};
   int j = 0;

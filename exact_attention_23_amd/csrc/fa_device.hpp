@@ -111,6 +111,26 @@ __device__ __forceinline__ int lds_off(int r, int c) {
   return r * ROW_BYTES + 16 * (c ^ swz);
 }
 
+// Byte offset of chunk c of row r in the forward's K and V tiles (rows of 2d
+// bytes). Besides one chunk of 16 consecutive rows per 16 lanes (the K
+// operand reads), the transpose reads of V^T straight from the V tile fetch 4
+// chunks of each of 4 consecutive rows (from a multiple of 4) per 32 lanes;
+// the swizzle puts those 4 rows in different 64-byte bank blocks of the
+// 256-byte window, which lds_off does not for 128- and 256-byte rows.
+template <int ROW_BYTES>
+__device__ __forceinline__ int tile_off(int r, int c) {
+  if constexpr (ROW_BYTES == 256) {
+    const int swz = ((r & 3) << 2) | ((r >> 2) & 3);  // rows r..r+3: blocks 0..3
+    return r * ROW_BYTES + 16 * (c ^ swz);
+  } else if constexpr (ROW_BYTES == 128) {
+    // two rows per window; rows r and r+2 take different 64-byte halves
+    const int swz = (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+    return r * ROW_BYTES + 16 * (c ^ swz);
+  } else {
+    return lds_off<ROW_BYTES>(r, c);
+  }
+}
+
 // One 16-byte-per-lane buffer load straight into LDS: lane l's bytes land at
 // LDS address lds_addr + 16*l. Written as inline asm so that the compiler does
 // not guard every LDS read with a wait for all such loads in flight; the

@@ -273,7 +273,7 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
   for (int i = 0; i < CPT; ++i) {
     const int sl = (wave * CPT + i) * 64 + lane;
     const int r = sl / CPR;
-    const int ch = (lds_off<2 * D>(r, sl % CPR) - r * (2 * D)) >> 4;  // logical chunk
+    const int ch = (tile_off<2 * D>(r, sl % CPR) - r * (2 * D)) >> 4;  // logical chunk
     const int kkey = (r & ~31) | lds_row_to_key(r & 31);
     k_goff[i] = kkey * krs + 16 * ch;
     v_goff[i] = r * vrs + 16 * ch;
@@ -303,7 +303,7 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
 #pragma unroll
   for (int t = 0; t < NSUB; ++t)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) k_roff[t][s] = lds_off<2 * D>(32 * t + r32, 2 * s + half);
+    for (int s = 0; s < KS; ++s) k_roff[t][s] = tile_off<2 * D>(32 * t + r32, 2 * s + half);
   // V transpose (once per tile per workgroup): transpose read i of this wave
   // covers, in 16-lane group g, the block of keys k0..k0+3 and d columns
   // d0..d0+15 of the V tile; lane x points at key k0 + x/4, columns
@@ -316,7 +316,7 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
     const int k0 = 4 * (G % (BN / 4)), d0 = 16 * (G / (BN / 4));
     const int x = lane & 15;
     const int col = d0 + 4 * (x & 3);
-    tr_src[i] = lds_off<2 * D>(k0 + (x >> 2), col >> 3) + 2 * (col & 7);
+    tr_src[i] = tile_off<2 * D>(k0 + (x >> 2), col >> 3) + 2 * (col & 7);
     tr_dst[i] = lds_off<2 * BN>(d0 + x, k0 >> 3) + 2 * (k0 & 7);
   }
   // V^T A-operand: row 32*dt + r32 (a d column), keys 32t + 16*half + 8*s2
@@ -355,9 +355,9 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
     const int row = tr_row + 32 * t + 8 * s2;
     const int col = tr_col + 32 * dt;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4*)(vs + lds_off<2 * D>(row, col >> 3) + 2 * (col & 7)));
+        (lds_i16x4*)(vs + tile_off<2 * D>(row, col >> 3) + 2 * (col & 7)));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4*)(vs + lds_off<2 * D>(row + 4, col >> 3) + 2 * (col & 7)));
+        (lds_i16x4*)(vs + tile_off<2 * D>(row + 4, col >> 3) + 2 * (col & 7)));
     const u32x2 wl = __builtin_bit_cast(u32x2, lo), wh = __builtin_bit_cast(u32x2, hi);
     return __builtin_bit_cast(vec, u32x4{wl[0], wl[1], wh[0], wh[1]});
   };
