@@ -621,6 +621,84 @@ def vector_rates(iters: int = 4096, blocks: int = 256 * 16):
     return res
 
 
+def _probe_lib():
+    import ctypes
+
+    from exact_attention_23_amd import build
+
+    lib = ctypes.CDLL(build.PROBE_LIB_PATH)
+    lib.fa_probe_matrix_rate.argtypes = [ctypes.c_int] * 2 + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_probe_matrix_rate.restype = ctypes.c_int
+    lib.fa_probe_coexec.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_probe_coexec.restype = ctypes.c_int
+    return lib
+
+
+def _time_launches(launch, reps: int = 3) -> float:
+    """Seconds per call of launch() (two warm-up calls, then `reps` timed)."""
+    import torch
+
+    for _ in range(2):
+        launch()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        launch()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) * 1e-3 / reps
+
+
+def matrix_rate(iters: int = 4096, blocks: int = 256 * 2):
+    """The rate of v_mfma_f32_32x32x16_f16 alone (4 independent accumulator
+    chains per wave, two waves per SIMD) from libfa_probe.so: the matrix-core
+    rate an attention kernel built on that instruction can reach on this
+    chip, against the published dense fp16 peak."""
+    import torch
+
+    import exact_attention_23_amd as fa
+
+    lib = _probe_lib()
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    stream = fa._current_stream(0)
+
+    def launch():
+        assert lib.fa_probe_matrix_rate(blocks, iters, out.data_ptr(), stream) == 0
+
+    sec = _time_launches(launch)
+    if not torch.isfinite(out).all():
+        raise RuntimeError("matrix probe produced non-finite values")
+    tflops = blocks * 4 * iters * 4 * 32768 / sec / 1e12
+    return {"instruction": "v_mfma_f32_32x32x16_f16", "tflops": round(tflops, 1),
+            "frac_of_published_peak": round(tflops / PEAK_MFMA_TFLOPS, 4)}
+
+
+def coexec(matrix_iters: int = 2048, vector_iters: int = 2048, blocks: int = 256):
+    """Whether the SIMDs overlap matrix and vector work of different waves
+    (libfa_probe.so's fa_probe_coexec): one wave per SIMD runs matrix chains,
+    another the softmax's vector steps; timed alone and together. both/sum
+    near 1 means the two kinds of work take turns, both/max near 1 that they
+    overlap."""
+    import torch
+
+    import exact_attention_23_amd as fa
+
+    lib = _probe_lib()
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda:0")
+    stream = fa._current_stream(0)
+    us = {}
+    for name, roles in (("matrix_only", 1), ("vector_only", 2), ("both", 3)):
+        def launch(roles=roles):
+            assert lib.fa_probe_coexec(roles, blocks, matrix_iters, vector_iters, out.data_ptr(), stream) == 0
+
+        us[name] = round(_time_launches(launch) * 1e6, 1)
+        if not torch.isfinite(out).all():
+            raise RuntimeError("co-execution probe produced non-finite values")
+    m, v, b = us["matrix_only"], us["vector_only"], us["both"]
+    return {"us": us, "both_over_sum": round(b / (m + v), 3), "both_over_max": round(b / max(m, v), 3)}
+
+
 def vector_roofline(w, us: float, rates):
     """The vector-unit bound of the forward on w: per score the softmax needs
     one FMA and one exp2 (the pair the probe times), so the pairs of all
@@ -897,6 +975,8 @@ def main(argv=None):
         rates = vector_rates()
         line["vector_rates"] = rates
         line["vector_roofline"] = vector_roofline(w, ms * 1e3, rates)
+        line["matrix_rate"] = matrix_rate()
+        line["coexec"] = coexec()
     if not args.no_bwd:
         # the backward pass of the same workload (a separate figure: the
         # headline value above is the forward's)

@@ -3,9 +3,11 @@
  * the attention library: the vector-unit throughput of the instructions the
  * forward's softmax step spends its time on (exp2 and fused multiply-add, the
  * per-score work of the online softmax in "FlashAttention 深度解读", section
- * 原理 2, and the kwkr.cn YOLO11 FlashAttention-2 article, section 1.2). The
- * benchmark turns the measured rates into a vector-unit bound for the
- * forward next to its matrix-core bound.
+ * 原理 2, and the kwkr.cn YOLO11 FlashAttention-2 article, section 1.2), the
+ * rate of its matrix instruction, and how far the two kinds of work overlap
+ * when different waves of one SIMD issue them. The benchmark turns the
+ * measured rates into a vector-unit bound for the forward next to its
+ * matrix-core bound.
  *
  * fa_probe_vector_rate - enqueue one kernel on `stream` that runs `iters`
  * iterations of `chains` independent dependency chains per thread, each
@@ -20,6 +22,25 @@
  * chains. Returns 0, or 1 for invalid arguments (op outside 0..2, blocks or
  * iters < 1, chains not 8, out NULL), or 2 when the launch fails. Time it
  * with events on `stream`.
+ *
+ * fa_probe_matrix_rate - enqueue one kernel of `blocks` workgroups of 256
+ * threads (4 waves); each wave runs `iters` steps of 4 independent
+ * v_mfma_f32_32x32x16_f16 chains (accumulators in vector registers, the
+ * forward's instruction and form): blocks * 4 * iters * 4 instructions of
+ * 32768 FLOP each. Each thread writes one float to out[blocks * 256]
+ * (caller-owned device memory). Returns 0, 1 for invalid arguments (blocks
+ * or iters < 1, out NULL), or 2 when the launch fails.
+ *
+ * fa_probe_coexec - enqueue one kernel of `blocks` workgroups of 512 threads
+ * (8 waves, two per SIMD). With bit 0 of `roles` set, waves 0-3 (one per
+ * SIMD) run `matrix_iters` steps of the matrix chains above; with bit 1 set,
+ * waves 4-7 run `vector_iters` steps of softmax-shaped vector work (32 values
+ * per lane, each step one v_fma_f32 and one v_exp_f32 per value and one
+ * v_cvt_pk_f16_f32 per pair). Timing roles 1, 2 and 3 shows whether the
+ * SIMDs overlap the two kinds of work (time of 3 near the larger of 1 and 2)
+ * or take them in turn (near their sum). Each thread writes one float to
+ * out[blocks * 512]. Returns 0, 1 for invalid arguments (roles outside 1..3,
+ * blocks or either count < 1, out NULL), or 2 when the launch fails.
  */
 #ifndef FA_PROBE_H_
 #define FA_PROBE_H_
@@ -33,6 +54,8 @@ extern "C" {
 enum fa_probe_op { FA_PROBE_EXP2 = 0, FA_PROBE_FMA = 1, FA_PROBE_MIX = 2 };
 
 int fa_probe_vector_rate(int op, int blocks, int iters, int chains, float* out, void* stream);
+int fa_probe_matrix_rate(int blocks, int iters, float* out, void* stream);
+int fa_probe_coexec(int roles, int blocks, int matrix_iters, int vector_iters, float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,10 @@ def _lib():
     lib = ctypes.CDLL(build.PROBE_LIB_PATH)
     lib.fa_probe_vector_rate.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
     lib.fa_probe_vector_rate.restype = ctypes.c_int
+    lib.fa_probe_matrix_rate.argtypes = [ctypes.c_int] * 2 + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_probe_matrix_rate.restype = ctypes.c_int
+    lib.fa_probe_coexec.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_probe_coexec.restype = ctypes.c_int
     return lib
 
 
@@ -24,7 +28,7 @@ def test_probe_exports_declared_symbols():
     with open(os.path.join(ROOT, "include", "fa_probe.h"), encoding="utf-8") as f:
         src = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
     names = re.findall(r"^\s*int\s+(fa_\w+)\s*\(", src, flags=re.M)
-    assert names == ["fa_probe_vector_rate"]
+    assert names == ["fa_probe_vector_rate", "fa_probe_matrix_rate", "fa_probe_coexec"]
     lib = _lib()
     for n in names:
         assert hasattr(lib, n)
@@ -35,6 +39,36 @@ def test_probe_exports_declared_symbols():
     (0, 1, 1, 4, 0x1000), (0, 1, 1, 8, 0)])
 def test_probe_rejects_bad_arguments_without_launching(op, blocks, iters, chains, out):
     assert _lib().fa_probe_vector_rate(op, blocks, iters, chains, out or None, None) == 1
+
+
+@pytest.mark.parametrize("blocks,iters,out", [(0, 1, 0x1000), (1, 0, 0x1000), (1, 1, 0)])
+def test_matrix_probe_rejects_bad_arguments_without_launching(blocks, iters, out):
+    assert _lib().fa_probe_matrix_rate(blocks, iters, out or None, None) == 1
+
+
+@pytest.mark.parametrize("roles,blocks,mi,vi,out", [
+    (0, 1, 1, 1, 0x1000), (4, 1, 1, 1, 0x1000), (1, 0, 1, 1, 0x1000), (1, 1, 0, 1, 0x1000),
+    (1, 1, 1, 0, 0x1000), (3, 1, 1, 1, 0)])
+def test_coexec_probe_rejects_bad_arguments_without_launching(roles, blocks, mi, vi, out):
+    assert _lib().fa_probe_coexec(roles, blocks, mi, vi, out or None, None) == 1
+
+
+@pytest.mark.gpu
+def test_matrix_and_coexec_probes_run():
+    import torch
+
+    from tests.gpu_util import require_gpu
+
+    require_gpu()
+    out = torch.zeros(8 * 512, device="cuda:0")
+    assert _lib().fa_probe_matrix_rate(8, 64, out.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    assert torch.isfinite(out[:8 * 256]).all() and bool((out[:8 * 256] > 0).all())
+    for roles in (1, 2, 3):
+        out.zero_()
+        assert _lib().fa_probe_coexec(roles, 8, 64, 64, out.data_ptr(), None) == 0
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all() and bool((out > 0).all())
 
 
 @pytest.mark.gpu
