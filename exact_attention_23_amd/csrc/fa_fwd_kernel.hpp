@@ -822,8 +822,9 @@ __device__ __forceinline__ bool fa_fwd_block(const Params& p, int head, int qb, 
 // copy, two workgroups share a CU by LDS (80 KB each), and the bf16 form would
 // otherwise take a few registers more than half the file; capped at two
 // waves it spills a dozen registers and runs 15% faster. Reading V^T
-// directly, three workgroups share a CU (48 KB each) and the cap is three
-// waves (one 32-row block per wave needs about 155 registers).
+// directly, three workgroups share a CU (32 KB each with the 2-stage ring)
+// and the cap is three waves (one 32-row block per wave needs about 150
+// registers).
 #ifndef FA_FWD_MIN_WAVES_D64_DIRECT
 #define FA_FWD_MIN_WAVES_D64_DIRECT 3
 #endif
