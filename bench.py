@@ -46,7 +46,8 @@ PEAK_HBM_GBS = 8000.0
 PEAK_MFMA_FP8_TFLOPS = 5033.2
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_23_amd", "csrc", f)
-                  for f in ("fa_device.hpp", "fa_fwd_kernel.hpp", "fa_fwd_short.hpp", "fa_api.hip")]
+                  for f in ("fa_device.hpp", "fa_fwd16.hpp", "fa_fwd_kernel.hpp", "fa_fwd_short.hpp",
+                            "fa_api.hip")]
 BWD_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_23_amd", "csrc", f)
                       for f in ("fa_device.hpp", "fa_bwd_kernel.hpp", "fa_bwd.hip")]
 FP8_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_23_amd", "csrc", f)
@@ -769,7 +770,7 @@ def write_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir:
             fetch += statistics.median(kf) * 1024 * f_scale
             write += statistics.median(kw) * 1024 * w_scale
     else:
-        kname = "fa_bwd_dkdv_kernel" if bwd else ("fa_fwd_fp8_kernel" if fp8 else "fa_fwd_kernel")
+        kname = "fa_bwd_dkdv_kernel" if bwd else ("fa_fwd_fp8_kernel" if fp8 else "fa_fwd16_kernel")
         kf = [v for k, v in _counter_rows(fetch_dir, "FETCH_SIZE") if kname in k]
         if not kf and not (bwd or fp8):  # a latency-bound size runs the short-range kernel
             kname = "fa_fwd_short_kernel"
@@ -784,7 +785,7 @@ def write_traffic(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir:
             rec = json.load(fh)
     except (OSError, ValueError):
         rec = {}
-    rec["about"] = ("HBM bytes per launch of fa_fwd_kernel (key: workload), of "
+    rec["about"] = ("HBM bytes per launch of fa_fwd16_kernel (key: workload), of "
                     "fa_bwd_dkdv_kernel (key: bwd:workload), of fa_fwd_fp8_kernel (key: "
                     "fp8:workload) and per call of the three standard-attention kernels (key: "
                     "std:workload) from rocprofv3 FETCH_SIZE and "

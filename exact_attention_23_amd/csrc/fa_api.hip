@@ -9,6 +9,7 @@
 
 #include "../../include/fa.h"
 #include "fa_host.hpp"
+#include "fa_fwd16.hpp"
 #include "fa_fwd_kernel.hpp"
 #include "fa_fwd_short.hpp"
 #include "fa_fwd_stream.hpp"
@@ -57,12 +58,39 @@ Variant make_variant(bool causal) {
 #define FA_TILES_D128 128, 64, 8, 1, 4, false, 0
 #endif
 
+// The tiled forward (fa_fwd16.hpp): 16x16x32 matrix instructions, NW waves of
+// QB 16-row query blocks, S LDS stages, per head width as (D, NW, QB, S); a
+// build can override them with -DFA_TILES16_D32=... etc. Against the 32x32x16
+// kernel above (fa_fwd_kernel.hpp, which the persistent form still uses),
+// same box, interleaved: 432 vs 438 us (yolo80b16), 353 vs 364 us (seq2048),
+// 2019 vs 2055 us (long16k). Measured and not kept: four query blocks per
+// wave (d = 32: 452 vs 442 us; d = 64, two waves per SIMD: 361 vs 355 us), a
+// 2-stage ring at d = 32 (432 vs 430) and a 3-stage one at d = 64 (365 vs
+// 352), constant ring stages at d = 128 (2057 vs 2019).
+#ifndef FA_TILES16_D32
+#define FA_TILES16_D32 32, 4, 2, 4
+#endif
+#ifndef FA_TILES16_D64
+#define FA_TILES16_D64 64, 4, 2, 2
+#endif
+#ifndef FA_TILES16_D128
+#define FA_TILES16_D128 128, 8, 2, 4
+#endif
+template <int D, int NW, int QB, int S, typename T>
+Variant make_variant16(bool causal) {
+  Variant v;
+  v.fn = causal ? fa::fa_fwd16_kernel<D, NW, QB, S, true, T> : fa::fa_fwd16_kernel<D, NW, QB, S, false, T>;
+  v.bm = 16 * QB * NW;
+  v.threads = 64 * NW;
+  return v;
+}
+
 template <typename T>
 Variant pick(int64_t d, bool causal) {
   switch (d) {
-    case 32: return make_variant<FA_TILES_D32, T>(causal);
-    case 64: return make_variant<FA_TILES_D64, T>(causal);
-    default: return make_variant<FA_TILES_D128, T>(causal);
+    case 32: return make_variant16<FA_TILES16_D32, T>(causal);
+    case 64: return make_variant16<FA_TILES16_D64, T>(causal);
+    default: return make_variant16<FA_TILES16_D128, T>(causal);
   }
 }
 

@@ -1,4 +1,8 @@
-// fa_fwd_kernel.hpp - the exact-attention forward kernel for gfx950 (CDNA4).
+// fa_fwd_kernel.hpp - the exact-attention forward block on 32x32x16 matrix
+// instructions for gfx950 (CDNA4), and the definitions the forward kernels
+// share (Params, Strides, work_item). The tiled forward now runs on the
+// 16x16x32 form (fa_fwd16.hpp); this block serves the persistent form
+// (fa_fwd_stream.hpp), which cuts a query block's key range into pieces.
 //
 // Method (kwkr.cn YOLO11 FlashAttention-2 article, section 1.2; "FlashAttention
 // 深度解读", section 原理 items 1-2 and the precision-handling paragraph;
@@ -20,12 +24,9 @@
 //   * K rows are placed in LDS in a permuted order so that accumulator
 //     register i of lane l holds key 16*(l/32)+i of its 32-key subtile. Those
 //     registers, rounded to fp16/bf16 in pairs (v_cvt_pk_*), are directly the
-//     B operand (P^T) of O^T += V^T P^T. Each V tile is transposed once per
-//     workgroup, one tile ahead, into a V^T buffer: ds_read_b64_tr_b16 hands
-//     each lane four consecutive keys of its own d column, which it stores as
-//     one 8-byte run. The waves then read their V^T operands with 16-byte LDS
-//     reads (the transpose read moves 8 bytes per lane and runs at about a
-//     third of the 16-byte read rate, so it is done once, not once per wave).
+//     B operand (P^T) of O^T += V^T P^T. The V^T operands come from the V
+//     tile itself, two ds_read_b64_tr_b16 transpose reads per operand (VT = 0),
+//     or from a copy transposed once per workgroup, one tile ahead (VT = 1).
 //   * O^T accumulates in fp32 MFMA accumulators: lane l holds d/2 elements of
 //     its query's output row.
 //   * Global reads are buffer loads whose range is one head's tensor, so rows
@@ -34,7 +35,7 @@
 //     ring of S stages, S-1 tiles ahead of the math, with no staging
 //     registers; each wave waits on its own loads (vmcnt) and one barrier per
 //     tile publishes a stage to the workgroup. LDS rows are XOR-swizzled in
-//     16-byte chunks against bank conflicts.
+//     16-byte chunks (tile_off) against bank conflicts.
 //   * exp is v_exp_f32 (2^x) on scores scaled by scale*log2(e), folded into one
 //     FMA with the reference maximum. The row sum that normalises O is taken
 //     from the same rounded P that enters the P V product, so the

@@ -55,7 +55,7 @@ def test_traffic_record_round_trip(tmp_path, monkeypatch):
     _write_counter_csv(tmp_path / "cf", [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 128 * kib)])
     _write_counter_csv(tmp_path / "cw", [("__amd_rocclr_copyBuffer", "WRITE_SIZE", 256 * kib)])
     # three dispatches of the forward kernel: median 50 MiB fetched, 20 MiB written (as counted)
-    name = "_ZN2fa13fa_fwd_kernelIL..."
+    name = "_ZN2fa15fa_fwd16_kernelIL..."
     _write_counter_csv(tmp_path / "f", [(name, "FETCH_SIZE", v * kib) for v in (49, 50, 60)])
     _write_counter_csv(tmp_path / "w", [(name, "WRITE_SIZE", v * kib) for v in (20, 20, 21)])
     ent = bench.write_traffic("wl", str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"),
