@@ -628,7 +628,7 @@ def _probe_lib():
     from exact_attention_23_amd import build
 
     lib = ctypes.CDLL(build.PROBE_LIB_PATH)
-    lib.fa_probe_matrix_rate.argtypes = [ctypes.c_int] * 2 + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_probe_matrix_rate.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_void_p]
     lib.fa_probe_matrix_rate.restype = ctypes.c_int
     lib.fa_probe_coexec.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
     lib.fa_probe_coexec.restype = ctypes.c_int
@@ -652,10 +652,11 @@ def _time_launches(launch, reps: int = 3) -> float:
 
 
 def matrix_rate(iters: int = 4096, blocks: int = 256 * 2):
-    """The rate of v_mfma_f32_32x32x16_f16 alone (4 independent accumulator
-    chains per wave, two waves per SIMD) from libfa_probe.so: the matrix-core
-    rate an attention kernel built on that instruction can reach on this
-    chip, against the published dense fp16 peak."""
+    """The rate of the matrix instructions alone (independent accumulator
+    chains, two waves per SIMD) from libfa_probe.so, for the 32x32x16 shape
+    and the 16x16x32 shape the tiled forward uses: what an attention kernel
+    built on them can reach on this chip, against the published dense fp16
+    peak."""
     import torch
 
     import exact_attention_23_amd as fa
@@ -663,16 +664,17 @@ def matrix_rate(iters: int = 4096, blocks: int = 256 * 2):
     lib = _probe_lib()
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
     stream = fa._current_stream(0)
+    res = {}
+    for name, shape in (("v_mfma_f32_32x32x16_f16", 0), ("v_mfma_f32_16x16x32_f16", 1)):
+        def launch(shape=shape):
+            assert lib.fa_probe_matrix_rate(shape, blocks, iters, out.data_ptr(), stream) == 0
 
-    def launch():
-        assert lib.fa_probe_matrix_rate(blocks, iters, out.data_ptr(), stream) == 0
-
-    sec = _time_launches(launch)
-    if not torch.isfinite(out).all():
-        raise RuntimeError("matrix probe produced non-finite values")
-    tflops = blocks * 4 * iters * 4 * 32768 / sec / 1e12
-    return {"instruction": "v_mfma_f32_32x32x16_f16", "tflops": round(tflops, 1),
-            "frac_of_published_peak": round(tflops / PEAK_MFMA_TFLOPS, 4)}
+        sec = _time_launches(launch)
+        if not torch.isfinite(out).all():
+            raise RuntimeError("matrix probe produced non-finite values")
+        tflops = blocks * 4 * iters * 131072 / sec / 1e12
+        res[name] = {"tflops": round(tflops, 1), "frac_of_published_peak": round(tflops / PEAK_MFMA_TFLOPS, 4)}
+    return res
 
 
 def coexec(matrix_iters: int = 2048, vector_iters: int = 2048, blocks: int = 256):

@@ -43,6 +43,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMatrixChains = 4;
 
@@ -74,8 +75,36 @@ __device__ __forceinline__ float matrix_chains(int iters) {
   return r;
 }
 
+// The 16x16x32 shape: 8 independent accumulator chains per wave, so a step
+// is the same FLOP count as a step of the 32x32x16 chains above.
+__device__ __forceinline__ float matrix_chains16(int iters) {
+  const int lane = threadIdx.x & 63;
+  f16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (_Float16)(0.001f * (float)((lane + i) & 31));
+    b[i] = (_Float16)(0.001f * (float)((lane + 3 * i) & 31));
+  }
+  f32x4 acc[2 * kMatrixChains];
+#pragma unroll
+  for (int c = 0; c < 2 * kMatrixChains; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[c][i] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < 2 * kMatrixChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[c], 0, 0, 0);
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int c = 0; c < 2 * kMatrixChains; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r += acc[c][i];
+  return r;
+}
+
+template <int SHAPE>
 __global__ __launch_bounds__(256) void matrix_kernel(int iters, float* out) {
-  out[(size_t)blockIdx.x * 256 + threadIdx.x] = matrix_chains(iters);
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = SHAPE == 0 ? matrix_chains(iters) : matrix_chains16(iters);
 }
 
 // Softmax-shaped vector work per step: for 32 values per lane, one FMA, one
@@ -120,11 +149,11 @@ __global__ __launch_bounds__(512) void coexec_kernel(int roles, int miters, int 
 
 }  // namespace
 
-extern "C" int fa_probe_matrix_rate(int blocks, int iters, float* out, void* stream) {
-  if (blocks < 1 || iters < 1 || out == nullptr) return 1;
+extern "C" int fa_probe_matrix_rate(int shape, int blocks, int iters, float* out, void* stream) {
+  if (shape < 0 || shape > 1 || blocks < 1 || iters < 1 || out == nullptr) return 1;
   void* args[] = {&iters, &out};
-  return hipLaunchKernel((const void*)matrix_kernel, dim3((unsigned)blocks), dim3(256), args, 0,
-                         (hipStream_t)stream) == hipSuccess ? 0 : 2;
+  const void* fn = shape == 0 ? (const void*)matrix_kernel<0> : (const void*)matrix_kernel<1>;
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, (hipStream_t)stream) == hipSuccess ? 0 : 2;
 }
 
 extern "C" int fa_probe_coexec(int roles, int blocks, int matrix_iters, int vector_iters, float* out,

@@ -24,12 +24,14 @@
  * with events on `stream`.
  *
  * fa_probe_matrix_rate - enqueue one kernel of `blocks` workgroups of 256
- * threads (4 waves); each wave runs `iters` steps of 4 independent
- * v_mfma_f32_32x32x16_f16 chains (accumulators in vector registers, the
- * forward's instruction and form): blocks * 4 * iters * 4 instructions of
- * 32768 FLOP each. Each thread writes one float to out[blocks * 256]
- * (caller-owned device memory). Returns 0, 1 for invalid arguments (blocks
- * or iters < 1, out NULL), or 2 when the launch fails.
+ * threads (4 waves); each wave runs `iters` steps of independent matrix
+ * instruction chains with accumulators in vector registers: shape 0, 4 chains
+ * of v_mfma_f32_32x32x16_f16 (32768 FLOP each); shape 1, 8 chains of
+ * v_mfma_f32_16x16x32_f16 (16384 FLOP each, the tiled forward's
+ * instruction). Either way a step is 131072 FLOP per wave, blocks * 4 * iters
+ * steps in all. Each thread writes one float to out[blocks * 256]
+ * (caller-owned device memory). Returns 0, 1 for invalid arguments (shape
+ * not 0 or 1, blocks or iters < 1, out NULL), or 2 when the launch fails.
  *
  * fa_probe_coexec - enqueue one kernel of `blocks` workgroups of 512 threads
  * (8 waves, two per SIMD). With bit 0 of `roles` set, waves 0-3 (one per
@@ -54,7 +56,7 @@ extern "C" {
 enum fa_probe_op { FA_PROBE_EXP2 = 0, FA_PROBE_FMA = 1, FA_PROBE_MIX = 2 };
 
 int fa_probe_vector_rate(int op, int blocks, int iters, int chains, float* out, void* stream);
-int fa_probe_matrix_rate(int blocks, int iters, float* out, void* stream);
+int fa_probe_matrix_rate(int shape, int blocks, int iters, float* out, void* stream);
 int fa_probe_coexec(int roles, int blocks, int matrix_iters, int vector_iters, float* out, void* stream);
 
 #ifdef __cplusplus

@@ -17,7 +17,7 @@ def _lib():
     lib = ctypes.CDLL(build.PROBE_LIB_PATH)
     lib.fa_probe_vector_rate.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
     lib.fa_probe_vector_rate.restype = ctypes.c_int
-    lib.fa_probe_matrix_rate.argtypes = [ctypes.c_int] * 2 + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_probe_matrix_rate.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_void_p]
     lib.fa_probe_matrix_rate.restype = ctypes.c_int
     lib.fa_probe_coexec.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
     lib.fa_probe_coexec.restype = ctypes.c_int
@@ -41,9 +41,10 @@ def test_probe_rejects_bad_arguments_without_launching(op, blocks, iters, chains
     assert _lib().fa_probe_vector_rate(op, blocks, iters, chains, out or None, None) == 1
 
 
-@pytest.mark.parametrize("blocks,iters,out", [(0, 1, 0x1000), (1, 0, 0x1000), (1, 1, 0)])
-def test_matrix_probe_rejects_bad_arguments_without_launching(blocks, iters, out):
-    assert _lib().fa_probe_matrix_rate(blocks, iters, out or None, None) == 1
+@pytest.mark.parametrize("shape,blocks,iters,out", [
+    (2, 1, 1, 0x1000), (-1, 1, 1, 0x1000), (0, 0, 1, 0x1000), (1, 1, 0, 0x1000), (0, 1, 1, 0)])
+def test_matrix_probe_rejects_bad_arguments_without_launching(shape, blocks, iters, out):
+    assert _lib().fa_probe_matrix_rate(shape, blocks, iters, out or None, None) == 1
 
 
 @pytest.mark.parametrize("roles,blocks,mi,vi,out", [
@@ -61,9 +62,11 @@ def test_matrix_and_coexec_probes_run():
 
     require_gpu()
     out = torch.zeros(8 * 512, device="cuda:0")
-    assert _lib().fa_probe_matrix_rate(8, 64, out.data_ptr(), None) == 0
-    torch.cuda.synchronize()
-    assert torch.isfinite(out[:8 * 256]).all() and bool((out[:8 * 256] > 0).all())
+    for shape in (0, 1):
+        out.zero_()
+        assert _lib().fa_probe_matrix_rate(shape, 8, 64, out.data_ptr(), None) == 0
+        torch.cuda.synchronize()
+        assert torch.isfinite(out[:8 * 256]).all() and bool((out[:8 * 256] > 0).all())
     for roles in (1, 2, 3):
         out.zero_()
         assert _lib().fa_probe_coexec(roles, 8, 64, 64, out.data_ptr(), None) == 0
