@@ -10,9 +10,10 @@
 //     dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q
 //
 // Three kernels, no atomics (every output element is summed in a fixed order):
-//   * fa_bwd_pre_kernel: per query row, D_i and LSE_i * log2(e) into a
+//   * fa_bwd_pre_kernel: per query row, -D_i and LSE_i * log2(e) into a
 //     workspace of 32-row records (rows past Nq get +inf and 0, so that they
-//     produce P = 0 downstream without any row masking).
+//     produce P = 0 downstream without any row masking). The dP products start
+//     their accumulation from -D, so dP - D costs no vector instruction.
 //   * fa_bwd_dkdv_kernel: one workgroup per block of BN = 32*NW keys; wave w
 //     owns 32 keys and keeps their K and V rows in VGPRs as MFMA B operands.
 //     It walks the head's query rows in tiles of 32 and accumulates dK and dV
@@ -72,7 +73,7 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* aux;    // [B*H][nrec][2][32] fp32: LSE*log2(e) (+inf past Nq), D (0 past Nq)
+  float* aux;    // [B*H][nrec][2][32] fp32: LSE*log2(e) (+inf past Nq), -D (0 past Nq)
   int B, H, Nq, Nk;
   int nrec;      // 32-row records per head: ceil(Nq / 32)
   int nblk;      // blocks per head (key blocks for dK/dV, query blocks for dQ)
@@ -106,7 +107,7 @@ __device__ __forceinline__ void bwd_work_item(const BwdParams& p, int bid, int& 
 }
 
 // ---------------------------------------------------------------------------
-// D_i = sum_c dO_ic O_ic and LSE_i * log2(e), per query row, into 32-row
+// -D_i = -sum_c dO_ic O_ic and LSE_i * log2(e), per query row, into 32-row
 // records. D/8 threads share a row, 16 bytes of O and dO each.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p) {
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p) {
   if (in && sub == 0) {
     float* rec = p.aux + ((size_t)head * p.nrec + (row >> 5)) * 64 + (row & 31);
     rec[0] = valid ? p.lse[(size_t)head * p.Nq + row] * kLog2e : __builtin_inff();
-    rec[32] = valid ? acc : 0.f;
+    rec[32] = valid ? -acc : 0.f;
   }
 }
 
@@ -379,17 +380,25 @@ __global__ __launch_bounds__(NW * 64, bwd_dkdv_min_waves(D)) void fa_bwd_dkdv_ke
         kb = kf[s];
       sa = M::run(a, kb, s == 0 ? f32x16{} : sa);
     }
+    // dP - D in one chain: the first dP MFMA starts from -D of the queries
+    // its registers hold (register 4a + b: query 8a + 4half + b)
+    f32x16 nd;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const f32x4 dz = *(const f32x4*)(ax + BM + 8 * a + 4 * half);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) nd[4 * a + b] = dz[b];
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const vec a = *(const vec*)(dos + a_off[s]);
-      dpa = M::run(a, vf[s], s == 0 ? f32x16{} : dpa);
+      dpa = M::run(a, vf[s], s == 0 ? nd : dpa);
     }
-    // P and dS in place of S and dP, four queries at a time: LSE*log2(e) and
-    // D of the lane's queries 8a + 4half + 0..3
+    // P and dS in place of S and dP - D, four queries at a time: LSE*log2(e)
+    // of the lane's queries 8a + 4half + 0..3
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const f32x4 lz = *(const f32x4*)(ax + 8 * a + 4 * half);
-      const f32x4 dz = *(const f32x4*)(ax + BM + 8 * a + 4 * half);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int i = 4 * a + b;
@@ -400,7 +409,7 @@ __global__ __launch_bounds__(NW * 64, bwd_dkdv_min_waves(D)) void fa_bwd_dkdv_ke
           pv = vis ? pv : 0.f;
         }
         sa[i] = pv;
-        dpa[i] = pv * (dpa[i] - dz[b]);
+        dpa[i] = pv * dpa[i];
       }
     }
     // P^T and dS^T as A operands: k-step c2 takes registers 8c2 .. 8c2+7.
@@ -543,12 +552,15 @@ __global__ __launch_bounds__(NW * 64, bwd_dq_min_waves(D)) void fa_bwd_dq_kernel
     dof[s] = __builtin_bit_cast(vec, __builtin_amdgcn_raw_buffer_load_b128(do_rsrc, off, 0, 0));
   }
   // Its LSE*log2(e) and D; rows past the records are padding (+inf, 0).
-  float lse2 = __builtin_inff(), dlt = 0.f;
+  float lse2 = __builtin_inff(), dlt = 0.f;  // dlt: -D
   if (q_row < p.nrec * 32) {
     const float* rec = p.aux + ((size_t)head * p.nrec + (q_row >> 5)) * 64 + (q_row & 31);
     lse2 = rec[0];
     dlt = rec[32];
   }
+  f32x16 ndv;  // d = 64: -D in every register, the start of each dP^T chain
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndv[i] = dlt;
 
   int kv_end = Nk;
   if (CAUSAL) {
@@ -666,7 +678,12 @@ __global__ __launch_bounds__(NW * 64, bwd_dq_min_waves(D)) void fa_bwd_dq_kernel
 #pragma unroll
     for (int s = 0; s < KS; ++s) sa = M::run(*(const vec*)(ks + a_off[t][s]), qf[s], s == 0 ? f32x16{} : sa);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) dpa = M::run(*(const vec*)(vs + a_off[t][s]), dof[s], s == 0 ? f32x16{} : dpa);
+    // d = 64: dP^T - D in one chain, the first MFMA starting from -D (the
+    // lane's query, in every register). At d = 32 (four waves per SIMD) and
+    // d = 128 the 16 registers of that start do not fit, and -D is added per
+    // score.
+    for (int s = 0; s < KS; ++s)
+      dpa = M::run(*(const vec*)(vs + a_off[t][s]), dof[s], s == 0 ? (D == 64 ? ndv : f32x16{}) : dpa);
     float ds[16];
     // keys j*BN + 32t + 16half + i are visible while i < lim
     int lim = 16;
@@ -678,7 +695,7 @@ __global__ __launch_bounds__(NW * 64, bwd_dq_min_waves(D)) void fa_bwd_dq_kernel
     for (int i = 0; i < 16; ++i) {
       float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, -lse2));
       if (MASK) pv = (i < lim) ? pv : 0.f;
-      ds[i] = pv * (dpa[i] - dlt);
+      ds[i] = D == 64 ? pv * dpa[i] : pv * (dpa[i] + dlt);
     }
     vec b[2];
 #pragma unroll

@@ -268,7 +268,7 @@ int64_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq);
  *   B, H, Nq, Nk, d, scale, causal, dtype, stream: as in fa_fwd
  *
  * dq, dk and dv must not overlap each other, any input or the workspace.
- * Work is enqueued on `stream` as three kernels (per-row D and the scaled
+ * Work is enqueued on `stream` as three kernels (per-row -D and the scaled
  * LSE into the workspace; dK and dV per block of keys; dQ per block of
  * query rows), so the workspace must stay allocated until they have run.
  * Returns FA_OK once enqueued, otherwise an fa_status code (all checks are
@@ -281,7 +281,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            float scale, int causal, int dtype, void* stream);
 
 /* Kernel selection for fa_bwd_ex, a bit mask. fa_bwd runs all three in this
- * order on one stream. FA_BWD_PRE fills the workspace (per-row D and the
+ * order on one stream. FA_BWD_PRE fills the workspace (per-row -D and the
  * scaled LSE); FA_BWD_DKDV and FA_BWD_DQ read it and are independent of each
  * other, so a caller may enqueue PRE, then DKDV and DQ on two streams that
  * both wait for PRE. */
