@@ -43,19 +43,24 @@
 
 namespace fa {
 
-// Byte offset of chunk c of row r in this kernel's K and V tiles. For rows of
-// 128 and 256 bytes lds_off already serves both read patterns. Rows of 64
-// bytes put rows r and r+4 on the same banks, which the transpose reads (8
-// consecutive rows per 32 lanes) would hit with lds_off's swizzle; here row
-// bit 2 flips chunk bit 1 and row bit 3 chunk bit 0 instead.
+// Byte offset of chunk c of row r in this kernel's K and V tiles: rows XOR-
+// swizzled in 16-byte chunks so that neither read pattern meets a bank
+// conflict on the 64 banks x 4 bytes of the LDS. A 16-byte read (the K
+// operand: lane x + 16g reads row x, chunk c + g) is served in four passes of
+// 16 lanes; lanes 0-7 go with lanes 24-31, 8-15 with 16-23, 32-39 with 56-63
+// and 40-47 with 48-55 (measured with SQ_LDS_BANK_CONFLICT on gfx950). A pass
+// thus reads rows 0-7 of one chunk and rows 8-15 of the next, so rows r and
+// r+8 take the same swizzle and the chunk parity keeps them apart. The
+// transpose reads (8 bytes, 32 lanes per pass: chunks c and c+1 of 8
+// consecutive rows) need the 8 rows to cover 16 distinct 16-byte bank groups.
 template <int ROW_BYTES>
 __device__ __forceinline__ int f16_off(int r, int c) {
-  if constexpr (ROW_BYTES == 64) {
-    const int swz = (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
-    return r * ROW_BYTES + 16 * (c ^ swz);
-  } else {
-    return lds_off<ROW_BYTES>(r, c);
-  }
+  static_assert(ROW_BYTES == 64 || ROW_BYTES == 128 || ROW_BYTES == 256, "row size");
+  int swz;
+  if constexpr (ROW_BYTES == 256) swz = (r & 7) << 1;               // one row per 256 bytes
+  else if constexpr (ROW_BYTES == 128) swz = ((r >> 1) & 3) << 1;   // two rows
+  else swz = ((r >> 2) & 1) << 1;                                   // four rows
+  return r * ROW_BYTES + 16 * (c ^ swz);
 }
 
 // One query block (head, qb) over the head's whole key range; strict as in
@@ -169,7 +174,7 @@ __device__ __forceinline__ bool fa_fwd16_block(const Params& p, int head, int qb
   };
 
   // K operand of key block kb, k-step s: row 16kb + x, chunk 4s + g. The
-  // swizzle depends on row bits 0-3 only, so the key block is an offset.
+  // swizzle depends on row bits 0-2 only, so the key block is an offset.
   int k_roff[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) k_roff[s] = f16_off<2 * D>(x, 4 * s + g);
