@@ -632,6 +632,8 @@ def _probe_lib():
     lib.fa_probe_matrix_rate.restype = ctypes.c_int
     lib.fa_probe_coexec.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
     lib.fa_probe_coexec.restype = ctypes.c_int
+    lib.fa_probe_coissue.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_probe_coissue.restype = ctypes.c_int
     return lib
 
 
@@ -700,6 +702,42 @@ def coexec(matrix_iters: int = 2048, vector_iters: int = 2048, blocks: int = 256
             raise RuntimeError("co-execution probe produced non-finite values")
     m, v, b = us["matrix_only"], us["vector_only"], us["both"]
     return {"us": us, "both_over_sum": round(b / (m + v), 3), "both_over_max": round(b / max(m, v), 3)}
+
+
+def coissue(iters: int = 2000, cus: int = 256):
+    """How far one wave's own matrix and vector instructions overlap
+    (libfa_probe.so's fa_probe_coissue), at one, two and four waves per SIMD:
+    per step 16 16x16x32 matrix instructions and the softmax's vector work on
+    32 values, timed alone, together in the compiler's order, and together
+    interleaved one matrix instruction to five vector instructions. Per
+    waves-per-SIMD setting: microseconds per launch, and `*_over_max`, the
+    combined time over the larger of the two alone (1 = complete overlap)."""
+    import torch
+
+    import exact_attention_23_amd as fa
+
+    lib = _probe_lib()
+    out = torch.empty(4 * cus * 256, dtype=torch.float32, device="cuda:0")
+    stream = fa._current_stream(0)
+    res = {}
+    for wps in (1, 2, 4):
+        blocks = cus * wps
+        us = {}
+        for name, mode in (("matrix_only", 1), ("vector_only", 2), ("both_compiler_order", 3),
+                           ("both_interleaved", 4)):
+            def launch(mode=mode, blocks=blocks):
+                assert lib.fa_probe_coissue(mode, blocks, iters, out.data_ptr(), stream) == 0
+
+            us[name] = round(_time_launches(launch) * 1e6, 1)
+            if not torch.isfinite(out[:blocks * 256]).all():
+                raise RuntimeError("co-issue probe produced non-finite values")
+        mx = max(us["matrix_only"], us["vector_only"])
+        res[f"{wps}_waves_per_simd"] = {
+            "us": us,
+            "compiler_order_over_max": round(us["both_compiler_order"] / mx, 3),
+            "interleaved_over_max": round(us["both_interleaved"] / mx, 3),
+        }
+    return res
 
 
 def vector_roofline(w, us: float, rates):
@@ -980,6 +1018,7 @@ def main(argv=None):
         line["vector_roofline"] = vector_roofline(w, ms * 1e3, rates)
         line["matrix_rate"] = matrix_rate()
         line["coexec"] = coexec()
+        line["coissue"] = coissue()
     if not args.no_bwd:
         # the backward pass of the same workload (a separate figure: the
         # headline value above is the forward's)

@@ -147,6 +147,63 @@ __global__ __launch_bounds__(512) void coexec_kernel(int roles, int miters, int 
   out[(size_t)blockIdx.x * 512 + threadIdx.x] = r;
 }
 
+// One wave per SIMD per workgroup of 256 threads; per step, 16 matrix
+// instructions (8 chains of v_mfma_f32_16x16x32_f16, two each) and/or the
+// vector steps' work on 32 values. MODE 1: matrix only; 2: vector only; 3:
+// both, in the compiler's order; 4: both, the instruction stream interleaved
+// one matrix instruction to five vector instructions (scheduling groups).
+template <int MODE>
+__global__ __launch_bounds__(256) void coissue_kernel(int iters, float* out) {
+  const int lane = threadIdx.x & 63;
+  f16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (_Float16)(0.001f * (float)(lane + i));
+    b[i] = (_Float16)(0.002f * (float)(i - lane));
+  }
+  f32x4 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float s[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) s[i] = 0.01f * (float)((lane + i) & 15);
+  uint32_t w = 0;
+  for (int it = 0; it < iters; ++it) {
+    if (MODE != 2) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[c], 0, 0, 0);
+    }
+    if (MODE != 1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i], -1.4426950f, -0.5f));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i + 1], -1.4426950f, -0.5f));
+        const f32x2 f = {p0, p1};
+        w ^= __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+        s[2 * i] = p0;
+        s[2 * i + 1] = p1;
+      }
+    }
+    if (MODE == 4) {
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix instruction
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five vector instructions
+      }
+    }
+  }
+  float r = (float)(w & 1);
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r += acc[c][i];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) r += s[i];
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = r;
+}
+
 }  // namespace
 
 extern "C" int fa_probe_matrix_rate(int shape, int blocks, int iters, float* out, void* stream) {
@@ -173,5 +230,15 @@ extern "C" int fa_probe_vector_rate(int op, int blocks, int iters, int chains, f
   const void* fn = op == FA_PROBE_EXP2 ? (const void*)probe_kernel<FA_PROBE_EXP2>
                    : op == FA_PROBE_FMA ? (const void*)probe_kernel<FA_PROBE_FMA>
                                         : (const void*)probe_kernel<FA_PROBE_MIX>;
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, (hipStream_t)stream) == hipSuccess ? 0 : 2;
+}
+
+extern "C" int fa_probe_coissue(int mode, int blocks, int iters, float* out, void* stream) {
+  if (mode < 1 || mode > 4 || blocks < 1 || iters < 1 || out == nullptr) return 1;
+  void* args[] = {&iters, &out};
+  const void* fn = mode == 1   ? (const void*)coissue_kernel<1>
+                   : mode == 2 ? (const void*)coissue_kernel<2>
+                   : mode == 3 ? (const void*)coissue_kernel<3>
+                               : (const void*)coissue_kernel<4>;
   return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, (hipStream_t)stream) == hipSuccess ? 0 : 2;
 }

@@ -5,7 +5,7 @@
  * per-score work of the online softmax in "FlashAttention 深度解读", section
  * 原理 2, and the kwkr.cn YOLO11 FlashAttention-2 article, section 1.2), the
  * rate of its matrix instruction, and how far the two kinds of work overlap
- * when different waves of one SIMD issue them. The benchmark turns the
+ * when different waves of one SIMD, or one wave, issue them. The benchmark turns the
  * measured rates into a vector-unit bound for the forward next to its
  * matrix-core bound.
  *
@@ -43,6 +43,19 @@
  * or take them in turn (near their sum). Each thread writes one float to
  * out[blocks * 512]. Returns 0, 1 for invalid arguments (roles outside 1..3,
  * blocks or either count < 1, out NULL), or 2 when the launch fails.
+ *
+ * fa_probe_coissue - enqueue one kernel of `blocks` workgroups of 256
+ * threads (4 waves, one per SIMD when blocks does not exceed the CUs; with
+ * 2x or 4x as many blocks, two or four waves share each SIMD). Each wave
+ * runs `iters` steps; a step holds, by `mode`: 1, 16 v_mfma_f32_16x16x32_f16
+ * (8 independent chains); 2, the vector work of one fa_probe_coexec vector
+ * step; 3, both in one wave, in the compiler's order; 4, both in one wave,
+ * the instruction stream interleaved one matrix instruction to five vector
+ * instructions. Timing modes 1-4 shows how far one wave's own matrix and
+ * vector instructions overlap, and how that compares with several waves
+ * sharing a SIMD. Each thread writes one float to out[blocks * 256]
+ * (caller-owned device memory). Returns 0, 1 for invalid arguments (mode
+ * outside 1..4, blocks or iters < 1, out NULL), or 2 when the launch fails.
  */
 #ifndef FA_PROBE_H_
 #define FA_PROBE_H_
@@ -58,6 +71,7 @@ enum fa_probe_op { FA_PROBE_EXP2 = 0, FA_PROBE_FMA = 1, FA_PROBE_MIX = 2 };
 int fa_probe_vector_rate(int op, int blocks, int iters, int chains, float* out, void* stream);
 int fa_probe_matrix_rate(int shape, int blocks, int iters, float* out, void* stream);
 int fa_probe_coexec(int roles, int blocks, int matrix_iters, int vector_iters, float* out, void* stream);
+int fa_probe_coissue(int mode, int blocks, int iters, float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,8 @@ def _lib():
     lib.fa_probe_matrix_rate.restype = ctypes.c_int
     lib.fa_probe_coexec.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
     lib.fa_probe_coexec.restype = ctypes.c_int
+    lib.fa_probe_coissue.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_probe_coissue.restype = ctypes.c_int
     return lib
 
 
@@ -28,7 +30,7 @@ def test_probe_exports_declared_symbols():
     with open(os.path.join(ROOT, "include", "fa_probe.h"), encoding="utf-8") as f:
         src = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
     names = re.findall(r"^\s*int\s+(fa_\w+)\s*\(", src, flags=re.M)
-    assert names == ["fa_probe_vector_rate", "fa_probe_matrix_rate", "fa_probe_coexec"]
+    assert names == ["fa_probe_vector_rate", "fa_probe_matrix_rate", "fa_probe_coexec", "fa_probe_coissue"]
     lib = _lib()
     for n in names:
         assert hasattr(lib, n)
@@ -54,6 +56,12 @@ def test_coexec_probe_rejects_bad_arguments_without_launching(roles, blocks, mi,
     assert _lib().fa_probe_coexec(roles, blocks, mi, vi, out or None, None) == 1
 
 
+@pytest.mark.parametrize("mode,blocks,iters,out", [
+    (0, 1, 1, 0x1000), (5, 1, 1, 0x1000), (1, 0, 1, 0x1000), (1, 1, 0, 0x1000), (4, 1, 1, 0)])
+def test_coissue_probe_rejects_bad_arguments_without_launching(mode, blocks, iters, out):
+    assert _lib().fa_probe_coissue(mode, blocks, iters, out or None, None) == 1
+
+
 @pytest.mark.gpu
 def test_matrix_and_coexec_probes_run():
     import torch
@@ -72,6 +80,12 @@ def test_matrix_and_coexec_probes_run():
         assert _lib().fa_probe_coexec(roles, 8, 64, 64, out.data_ptr(), None) == 0
         torch.cuda.synchronize()
         assert torch.isfinite(out).all() and bool((out > 0).all())
+    for mode in (1, 2, 3, 4):
+        out.zero_()
+        assert _lib().fa_probe_coissue(mode, 8, 64, out.data_ptr(), None) == 0
+        torch.cuda.synchronize()
+        # the matrix chains sum to negative values; every thread wrote a finite one
+        assert torch.isfinite(out[:8 * 256]).all() and bool((out[:8 * 256] != 0).all())
 
 
 @pytest.mark.gpu
