@@ -305,6 +305,14 @@ __device__ __forceinline__ bool fa_fwd16_block(const Params& p, int head, int qb
       }
   };
 
+  // P V of query block qb2 alone (its V^T operands read for it only)
+  auto pv_block = [&](int st, int qb2) {
+    const char* vs = smem[st][1];
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[qb2][db] = M::sel_sum(vt_op(vs, cs, db), pf[cs][qb2], oacc[qb2][db]);
+  };
   int first_masked = (Nk % BN == 0) ? t_hi : Nk / BN;
   if (CAUSAL) {
     const int diag = (qb * BM) / BN;
@@ -331,6 +339,29 @@ __device__ __forceinline__ bool fa_fwd16_block(const Params& p, int head, int qb
     wait_vmcnt<PENDING>();
     __syncthreads();
   };
+  // Unmasked tile of the optimistic pass after the first (no row-sum test),
+  // d = 128: P V of query block q-1 is issued among the exponentials of
+  // block q, so that one wave's matrix and vector instructions overlap (the
+  // two waves of a SIMD run in lockstep there); the V^T operands are read
+  // once per block instead of once for all blocks.
+  auto tile_split = [&](int j, int st) {
+    issue(j + S - 1, (st + S - 1) % S);
+    qk_step(st);
+    exp_block(0, -m_run[0]);
+#pragma unroll
+    for (int qb2 = 1; qb2 < QB; ++qb2) {
+      pv_block(st, qb2 - 1);
+      exp_block(qb2, -m_run[qb2]);
+    }
+#pragma unroll
+    for (int qb2 = 0; qb2 < QB; ++qb2) {
+      l_run[qb2] += psum[qb2];
+      if constexpr (M::kLse32) l32_run[qb2] += ps32[qb2];
+    }
+    pv_block(st, QB - 1);
+    wait_vmcnt<PENDING>();
+    __syncthreads();
+  };
   auto stage = [&](int jj) { return (jj - t_lo) % S; };
   int j = t_lo;
   // d <= 64: unmasked tiles S at a time, so every ring stage is a constant
@@ -341,6 +372,11 @@ __device__ __forceinline__ bool fa_fwd16_block(const Params& p, int head, int qb
       [&]<int... I>(std::integer_sequence<int, I...>) {
         (tile(unmasked, j + I, I), ...);
       }(std::make_integer_sequence<int, S>{});
+  if constexpr (D == 128)
+    if (!strict && j < first_masked) {
+      tile(unmasked, j, stage(j));  // the first tile sets the reference maximum
+      for (++j; j < first_masked; ++j) tile_split(j, stage(j));
+    }
   for (; j < first_masked; ++j) tile(unmasked, j, stage(j));
   for (; j < t_hi && !beyond_rows(j); ++j) tile(masked, j, stage(j));
   for (; j < t_hi; ++j) {  // past this wave's rows: its share of loads and barriers
