@@ -58,6 +58,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "fa_device.hpp"
 
@@ -278,8 +279,7 @@ __global__ __launch_bounds__(NW * 64, bwd_dkdv_min_waves(D)) void fa_bwd_dkdv_ke
   const uint32_t lds_ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&ring[0][0][0];
   const uint32_t lds_aux = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&auxs[0][0];
   constexpr uint32_t kOutOfRange = 0x40000000u;
-  auto issue = [&](int j) {
-    const int st = j % S;
+  auto issue = [&](int j, int st) {  // tile j into ring stage st (= j % S)
     const bool live = j < ntiles;
     const uint32_t gb = live ? (uint32_t)((t0 + j) * TILE) : kOutOfRange;
 #pragma unroll
@@ -359,14 +359,14 @@ __global__ __launch_bounds__(NW * 64, bwd_dkdv_min_waves(D)) void fa_bwd_dkdv_ke
   };
 
   // ---- one query tile
-  auto tile = [&](auto mask_tag, int j) {
+  auto tile = [&](auto mask_tag, int j, int st) {  // tile j, in ring stage st
     constexpr bool MASK = decltype(mask_tag)::value;
     const int i0 = (t0 + j) * BM;
     // Causal: a wave whose first key is after the tile's last row adds zeros.
     if (MASK && CAUSAL && kw0 > i0 + BM - 1) return;
-    const char* qs = &ring[j % S][0][0];
-    const char* dos = &ring[j % S][1][0];
-    const float* ax = auxs[j % S];
+    const char* qs = &ring[st][0][0];
+    const char* dos = &ring[st][1][0];
+    const float* ax = auxs[st];
     const char* qt = &trb[DIRECT ? 0 : (j & 1)][0][0];
     const char* dot = &trb[DIRECT ? 0 : (j & 1)][1][0];
     f32x16 sa, dpa;
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(NW * 64, bwd_dkdv_min_waves(D)) void fa_bwd_dkdv_ke
     // prologue: tiles 0..S-2 requested; tile 0 landed (copy path: tiles 0
     // and 1, and tile 0 transposed)
 #pragma unroll
-    for (int t = 0; t < S - 1; ++t) issue(t);
+    for (int t = 0; t < S - 1; ++t) issue(t, t);
     wait_vmcnt<PENDING>();
     __syncthreads();
     if constexpr (!DIRECT) {
@@ -449,24 +449,29 @@ __global__ __launch_bounds__(NW * 64, bwd_dkdv_min_waves(D)) void fa_bwd_dkdv_ke
     }
     const auto unmasked = std::integral_constant<bool, false>{};
     const auto masked = std::integral_constant<bool, true>{};
-    // Step j: request tile j+S-1 into the stage of tile j-1, (copy path)
-    // transpose tile j+1, compute tile j; then wait until the next tile to
-    // read has landed and meet at the barrier.
+    // Step j (tile j in ring stage st = j % S): request tile j+S-1 into the
+    // stage of tile j-1, (copy path) transpose tile j+1, compute tile j; then
+    // wait until the next tile to read has landed and meet at the barrier.
+    auto step = [&](auto mask_tag, int j, int st) {
+      issue(j + S - 1, (st + S - 1) % S);
+      transpose(j + 1);
+      tile(mask_tag, j, st);
+      wait_vmcnt<PENDING>();
+      __syncthreads();
+    };
     int j = 0;
-    for (; j < first_free; ++j) {
-      issue(j + S - 1);
-      transpose(j + 1);
-      tile(masked, j);
-      wait_vmcnt<PENDING>();
-      __syncthreads();
+    for (; j < first_free; ++j) step(masked, j, j % S);
+    // Direct path: unmasked tiles S at a time from a tile in stage 0, so the
+    // stages are constants and the LDS operand addresses are per-lane bases
+    // plus immediates.
+    if constexpr (DIRECT) {
+      for (; j < ntiles && j % S != 0; ++j) step(unmasked, j, j % S);
+      for (; j + S <= ntiles; j += S)
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+          (step(unmasked, j + I, I), ...);
+        }(std::make_integer_sequence<int, S>{});
     }
-    for (; j < ntiles; ++j) {
-      issue(j + S - 1);
-      transpose(j + 1);
-      tile(unmasked, j);
-      wait_vmcnt<PENDING>();
-      __syncthreads();
-    }
+    for (; j < ntiles; ++j) step(unmasked, j, j % S);
   }
 
   // ---- epilogue: dK = scale * acc, dV = acc; lane l holds column 32dt + l%32
@@ -594,8 +599,7 @@ __global__ __launch_bounds__(NW * 64, bwd_dq_min_waves(D)) void fa_bwd_dq_kernel
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&smem[0][0][0];
   constexpr uint32_t kOutOfRange = 0x40000000u;
-  auto issue = [&](int t) {
-    const int st = t % S;
+  auto issue = [&](int t, int st) {  // tile t into ring stage st (= t % S)
     const uint32_t gb = t < ntiles ? (uint32_t)(t * TILE) : kOutOfRange;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
@@ -669,10 +673,10 @@ __global__ __launch_bounds__(NW * 64, bwd_dq_min_waves(D)) void fa_bwd_dq_kernel
     return __builtin_bit_cast(vec, u32x4{wl[0], wl[1], wh[0], wh[1]});
   };
 
-  auto unit = [&](auto mask_tag, int j, int t) {
+  auto unit = [&](auto mask_tag, int j, int t, int st) {  // unit t of tile j, in ring stage st
     constexpr bool MASK = decltype(mask_tag)::value;
-    const char* ks = smem[j % S][0];
-    const char* vs = smem[j % S][1];
+    const char* ks = smem[st][0];
+    const char* vs = smem[st][1];
     const char* kt = kts[DIRECT ? 0 : (j & 1)];
     f32x16 sa, dpa;
 #pragma unroll
@@ -716,7 +720,7 @@ __global__ __launch_bounds__(NW * 64, bwd_dq_min_waves(D)) void fa_bwd_dq_kernel
   // prologue: tiles 0..S-2 requested, tile 0 landed (copy path: tiles 0
   // and 1, and K^T of tile 0 written)
 #pragma unroll
-  for (int t = 0; t < S - 1; ++t) issue(t);
+  for (int t = 0; t < S - 1; ++t) issue(t, t);
   wait_vmcnt<PENDING>();
   __syncthreads();
   if constexpr (!DIRECT) {
@@ -725,29 +729,31 @@ __global__ __launch_bounds__(NW * 64, bwd_dq_min_waves(D)) void fa_bwd_dq_kernel
   }
   const auto unmasked = std::integral_constant<bool, false>{};
   const auto masked = std::integral_constant<bool, true>{};
-  int j = 0;
-  for (; j < first_masked; ++j) {
-    issue(j + S - 1);
+  // Step j (tile j in ring stage st = j % S), as in the dK/dV kernel.
+  auto step = [&](auto mask_tag, int j, int st) {
+    issue(j + S - 1, (st + S - 1) % S);
     transpose_k(j + 1);
-    unit(unmasked, j, 0);
-    unit(unmasked, j, 1);
+    unit(mask_tag, j, 0, st);
+    unit(mask_tag, j, 1, st);
     wait_vmcnt<PENDING>();
     __syncthreads();
-  }
+  };
+  int j = 0;
+  // d = 32: unmasked tiles S at a time, ring stages as constants (at d = 64
+  // the unrolled loop ran 4% slower).
+  if constexpr (D == 32)
+    for (; j + S <= first_masked; j += S)
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        (step(unmasked, j + I, I), ...);
+      }(std::make_integer_sequence<int, S>{});
+  for (; j < first_masked; ++j) step(unmasked, j, j % S);
   // Causal: tiles whose first key comes after this wave's last row add
   // nothing to its rows; the wave only takes its share of their loads,
   // transposes and barriers.
   const int wave_last_row = qb * BM + 32 * wave + 31;
-  for (; j < ntiles && !(CAUSAL && j * BN > wave_last_row); ++j) {
-    issue(j + S - 1);
-    transpose_k(j + 1);
-    unit(masked, j, 0);
-    unit(masked, j, 1);
-    wait_vmcnt<PENDING>();
-    __syncthreads();
-  }
+  for (; j < ntiles && !(CAUSAL && j * BN > wave_last_row); ++j) step(masked, j, j % S);
   for (; j < ntiles; ++j) {
-    issue(j + S - 1);
+    issue(j + S - 1, (j + S - 1) % S);
     transpose_k(j + 1);
     wait_vmcnt<PENDING>();
     __syncthreads();
