@@ -34,6 +34,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "fa_device.hpp"
 #include "fa_fwd_kernel.hpp"
@@ -166,8 +167,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_fp8_kernel(Fp8Params pp) {
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&smem[0][0][0];
   constexpr uint32_t kOutOfRange = 0x40000000u;
-  auto issue = [&](int t) {
-    const int st = t % S;
+  auto issue = [&](int t, int st) {  // tile t into ring stage st (= t % S)
     const uint32_t gb = t < ntiles ? (uint32_t)(t * TILE) : kOutOfRange;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
@@ -190,8 +190,8 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_fp8_kernel(Fp8Params pp) {
     tr_src[i] = lds_off<D>(k0 + (x >> 1), d0 >> 4) + 8 * (x & 1);
     tr_dst[i] = lds_off<BN>(d0 + x, k0 >> 4) + (k0 & 15);
   }
-  auto transpose_v = [&](int j) {
-    const char* src = smem[j % S][1];
+  auto transpose_v = [&](int j, int st) {  // tile j, in ring stage st
+    const char* src = smem[st][1];
     char* dst = vts[j & 1];
     i32x2 blk[TPW];
 #pragma unroll
@@ -218,9 +218,9 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_fp8_kernel(Fp8Params pp) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) v_off[dt][t] = lds_off<BN>(32 * dt + r32, 2 * t + half);
 
-  auto tile = [&](auto mask_tag, int j) {
+  auto tile = [&](auto mask_tag, int j, int st) {  // tile j, in ring stage st
     constexpr bool MASK = decltype(mask_tag)::value;
-    const char* ks = smem[j % S][0];
+    const char* ks = smem[st][0];
     const char* vt = vts[j & 1];
     f32x16 sacc[2];
 #pragma unroll
@@ -285,35 +285,39 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_fp8_kernel(Fp8Params pp) {
 
   // prologue: tiles 0..S-2 requested, V^T of tile 0 written
 #pragma unroll
-  for (int t = 0; t < S - 1; ++t) issue(t);
+  for (int t = 0; t < S - 1; ++t) issue(t, t);
   wait_vmcnt<PENDING>();
   __syncthreads();
-  transpose_v(0);
+  transpose_v(0, 0);
   __syncthreads();
   const auto unmasked = std::integral_constant<bool, false>{};
   const auto masked = std::integral_constant<bool, true>{};
-  int j = 0;
-  for (; j < first_masked; ++j) {
-    issue(j + S - 1);
-    transpose_v(j + 1);
-    tile(unmasked, j);
+  // Step j (tile j in ring stage st = j % S): request tile j+S-1 into the
+  // stage of tile j-1, transpose tile j+1, compute tile j, wait for the next
+  // tile and meet at the barrier.
+  auto step = [&](auto mask_tag, int j, int st) {
+    issue(j + S - 1, (st + S - 1) % S);
+    transpose_v(j + 1, (st + 1) % S);
+    tile(mask_tag, j, st);
     wait_vmcnt<PENDING>();
     __syncthreads();
-  }
+  };
+  int j = 0;
+  // Unmasked tiles S at a time: the ring stages (and V^T buffers) are
+  // constants, so LDS operand addresses are per-lane bases plus immediates.
+  for (; j + S <= first_masked; j += S)
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (step(unmasked, j + I, I), ...);
+    }(std::make_integer_sequence<int, S>{});
+  for (; j < first_masked; ++j) step(unmasked, j, j % S);
   // Causal: tiles whose first key comes after this wave's last row add
   // nothing to its rows; the wave only takes its share of their loads,
   // transposes and barriers.
   const int wave_last_row = qb * BM + 32 * wave + 31;
-  for (; j < ntiles && !(CAUSAL && j * BN > wave_last_row); ++j) {
-    issue(j + S - 1);
-    transpose_v(j + 1);
-    tile(masked, j);
-    wait_vmcnt<PENDING>();
-    __syncthreads();
-  }
+  for (; j < ntiles && !(CAUSAL && j * BN > wave_last_row); ++j) step(masked, j, j % S);
   for (; j < ntiles; ++j) {
-    issue(j + S - 1);
-    transpose_v(j + 1);
+    issue(j + S - 1, (j + S - 1) % S);
+    transpose_v(j + 1, (j + 1) % S);
     wait_vmcnt<PENDING>();
     __syncthreads();
   }
