@@ -18,7 +18,10 @@ measured HBM bytes), the FP8 forward on the two long workloads, the standard
 (unfused) attention against the fused forward on the 2048-token workload, and
 the vector-unit rates of exp2 and FMA with the vector-unit bound they set on
 the d = 32 workload. The FP8 records cover the three workloads of 2048 tokens
-and more.
+and more. The backward pass is timed on the headline workload (`backward`) and
+on the other two long workloads (`backward_workloads`); the matrix-rate,
+co-execution and co-issue probes report what the matrix and vector units reach
+on their own and together.
 
 The CPU baseline times the fp64 oracle, unmodified, on the host's cores: one
 worker process per core (at most 16), BLAS at one thread each, over whole
@@ -1024,6 +1027,16 @@ def main(argv=None):
         # headline value above is the forward's)
         bms, bper = time_bwd(w, max(args.steps // 2, 5), max(args.warmup // 2, 2), args.settle_ms)
         line["backward"] = bwd_record(w, bms, bper)
+        if not args.no_extras:
+            # the backward of the other long workloads, each on its own
+            # inputs, so every head width's backward is measured in this run
+            line["backward_workloads"] = {}
+            for n in ("seq2048", "long16k"):
+                if n == w.name:
+                    continue
+                bw = WORKLOADS[n]
+                bms2, bper2 = time_bwd(bw, max(args.steps // 2, 5), max(args.warmup // 2, 2), args.settle_ms)
+                line["backward_workloads"][n] = bwd_record(bw, bms2, bper2)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
