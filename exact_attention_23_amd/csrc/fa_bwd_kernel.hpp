@@ -196,6 +196,10 @@ __global__ __launch_bounds__(NW * 64, bwd_dkdv_min_waves(D)) void fa_bwd_dkdv_ke
   // are full there); each wave reads back only its own 32 rows.
   constexpr bool K_LDS = FA_BWD_K_LDS && D == 128;
   __shared__ __attribute__((aligned(1024))) char kls[K_LDS ? 32 * NW : 1][K_LDS ? 2 * D : 16];
+  // At d = 64 a tile computes P, and its dV products, before dP - D: the
+  // exponentials then overlap matrix work of the same wave (2.5% faster
+  // there; at d = 32 and 128 it ran slower, and at 128 it spills).
+  constexpr bool P_FIRST = D == 64;
 
   int head, kb;
   bwd_work_item<false>(p, blockIdx.x, head, kb);
@@ -380,60 +384,129 @@ __global__ __launch_bounds__(NW * 64, bwd_dkdv_min_waves(D)) void fa_bwd_dkdv_ke
         kb = kf[s];
       sa = M::run(a, kb, s == 0 ? f32x16{} : sa);
     }
-    // dP - D in one chain: the first dP MFMA starts from -D of the queries
-    // its registers hold (register 4a + b: query 8a + 4half + b)
-    f32x16 nd;
+    if constexpr (P_FIRST) {
+      // P first, four queries at a time (LSE*log2(e) of the lane's queries
+      // 8a + 4half + 0..3), and dV += P^T dO from it, so that the vector work
+      // of P and the matrix work of dP - D and dV can overlap in this wave
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const f32x4 dz = *(const f32x4*)(ax + BM + 8 * a + 4 * half);
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 lz = *(const f32x4*)(ax + 8 * a + 4 * half);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) nd[4 * a + b] = dz[b];
-    }
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const vec a = *(const vec*)(dos + a_off[s]);
-      dpa = M::run(a, vf[s], s == 0 ? nd : dpa);
-    }
-    // P and dS in place of S and dP - D, four queries at a time: LSE*log2(e)
-    // of the lane's queries 8a + 4half + 0..3
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const f32x4 lz = *(const f32x4*)(ax + 8 * a + 4 * half);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int i = 4 * a + b;
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, -lz[b]));
-        if (MASK) {
-          const int qi = i0 + 8 * a + 4 * half + b;
-          const bool vis = key < Nk && (!CAUSAL || key <= qi);
-          pv = vis ? pv : 0.f;
+        for (int b = 0; b < 4; ++b) {
+          const int i = 4 * a + b;
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, -lz[b]));
+          if (MASK) {
+            const int qi = i0 + 8 * a + 4 * half + b;
+            const bool vis = key < Nk && (!CAUSAL || key <= qi);
+            pv = vis ? pv : 0.f;
+          }
+          sa[i] = pv;
         }
-        sa[i] = pv;
-        dpa[i] = pv * dpa[i];
       }
+      vec pa[2], da[2];
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        u32x4 wp;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          wp[m] = __builtin_bit_cast(uint32_t, M::cvt(sa[8 * c2 + 2 * m], sa[8 * c2 + 2 * m + 1]));
+        pa[c2] = __builtin_bit_cast(vec, wp);
+      }
+      // dP - D in one chain: the first dP MFMA starts from -D of the queries
+      // its registers hold (register 4a + b: query 8a + 4half + b)
+      f32x16 nd;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 dz = *(const f32x4*)(ax + BM + 8 * a + 4 * half);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) nd[4 * a + b] = dz[b];
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const vec a = *(const vec*)(dos + a_off[s]);
+        dpa = M::run(a, vf[s], s == 0 ? nd : dpa);
+      }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const vec bo = DIRECT ? b_direct(dos, c2, dt) : *(const vec*)(dot + b_off[dt][c2]);
+          dv[dt] = M::run(pa[c2], bo, dv[dt]);
+        }
+      // dS = P (dP - D)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dpa[i] = sa[i] * dpa[i];
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        u32x4 wd;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          wd[m] = __builtin_bit_cast(uint32_t, M::cvt(dpa[8 * c2 + 2 * m], dpa[8 * c2 + 2 * m + 1]));
+        da[c2] = __builtin_bit_cast(vec, wd);
+      }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const vec bq = DIRECT ? b_direct(qs, c2, dt) : *(const vec*)(qt + b_off[dt][c2]);
+          dk[dt] = M::run(da[c2], bq, dk[dt]);
+        }
+    } else {
+      // dP - D in one chain: the first dP MFMA starts from -D of the queries
+      // its registers hold (register 4a + b: query 8a + 4half + b)
+      f32x16 nd;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 dz = *(const f32x4*)(ax + BM + 8 * a + 4 * half);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) nd[4 * a + b] = dz[b];
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const vec a = *(const vec*)(dos + a_off[s]);
+        dpa = M::run(a, vf[s], s == 0 ? nd : dpa);
+      }
+      // P and dS in place of S and dP - D, four queries at a time: LSE*log2(e)
+      // of the lane's queries 8a + 4half + 0..3
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 lz = *(const f32x4*)(ax + 8 * a + 4 * half);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int i = 4 * a + b;
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, -lz[b]));
+          if (MASK) {
+            const int qi = i0 + 8 * a + 4 * half + b;
+            const bool vis = key < Nk && (!CAUSAL || key <= qi);
+            pv = vis ? pv : 0.f;
+          }
+          sa[i] = pv;
+          dpa[i] = pv * dpa[i];
+        }
+      }
+      // P^T and dS^T as A operands: k-step c2 takes registers 8c2 .. 8c2+7.
+      vec pa[2], da[2];
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        u32x4 wp, wd;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          wp[m] = __builtin_bit_cast(uint32_t, M::cvt(sa[8 * c2 + 2 * m], sa[8 * c2 + 2 * m + 1]));
+          wd[m] = __builtin_bit_cast(uint32_t, M::cvt(dpa[8 * c2 + 2 * m], dpa[8 * c2 + 2 * m + 1]));
+        }
+        pa[c2] = __builtin_bit_cast(vec, wp);
+        da[c2] = __builtin_bit_cast(vec, wd);
+      }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const vec bo = DIRECT ? b_direct(dos, c2, dt) : *(const vec*)(dot + b_off[dt][c2]);
+          const vec bq = DIRECT ? b_direct(qs, c2, dt) : *(const vec*)(qt + b_off[dt][c2]);
+          dv[dt] = M::run(pa[c2], bo, dv[dt]);
+          dk[dt] = M::run(da[c2], bq, dk[dt]);
+        }
     }
-    // P^T and dS^T as A operands: k-step c2 takes registers 8c2 .. 8c2+7.
-    vec pa[2], da[2];
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      u32x4 wp, wd;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        wp[m] = __builtin_bit_cast(uint32_t, M::cvt(sa[8 * c2 + 2 * m], sa[8 * c2 + 2 * m + 1]));
-        wd[m] = __builtin_bit_cast(uint32_t, M::cvt(dpa[8 * c2 + 2 * m], dpa[8 * c2 + 2 * m + 1]));
-      }
-      pa[c2] = __builtin_bit_cast(vec, wp);
-      da[c2] = __builtin_bit_cast(vec, wd);
-    }
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const vec bo = DIRECT ? b_direct(dos, c2, dt) : *(const vec*)(dot + b_off[dt][c2]);
-        const vec bq = DIRECT ? b_direct(qs, c2, dt) : *(const vec*)(qt + b_off[dt][c2]);
-        dv[dt] = M::run(pa[c2], bo, dv[dt]);
-        dk[dt] = M::run(da[c2], bq, dk[dt]);
-      }
   };
 
   if (ntiles > 0) {
