@@ -363,6 +363,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
                                                : pick_short<__bf16>(d, causal != 0).fn;
     p.num_qb = (int)((Nq + 31) / 32);
     p.total = (int)short_total;
+    p.xcd_q = (int)(short_total / 8);
+    p.xcd_r = (int)(short_total % 8);
     e = hipLaunchKernel((const void*)fn, dim3((unsigned)short_total), dim3((unsigned)(64 * key_tiles)),
                         args, 0, (hipStream_t)stream);
   } else {

@@ -55,8 +55,13 @@ __global__ __launch_bounds__(1024) void fa_fwd_short_kernel(Params p) {
   // per wave and row: reference, normaliser sum, log-sum-exp sum
   __shared__ float s_m[MAXW][32], s_l[MAXW][32], s_l32[MAXW][32];
 
-  const int head = blockIdx.x / p.num_qb;
-  const int qb = blockIdx.x - head * p.num_qb;
+  // Workgroup w runs on XCD w % 8 (round-robin dispatch); number the blocks
+  // contiguously per XCD so that a head's blocks share one or two XCDs and
+  // their K and V reads are served by one L2 instead of every XCD's.
+  const int xcd = blockIdx.x & 7;
+  const int L = xcd * p.xcd_q + (xcd < p.xcd_r ? xcd : p.xcd_r) + (blockIdx.x >> 3);
+  const int head = L / p.num_qb;
+  const int qb = L - head * p.num_qb;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // scalar wave index: every per-wave choice below is a scalar branch
