@@ -50,11 +50,12 @@ PEAK_MFMA_FP8_TFLOPS = 5033.2
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_23_amd", "csrc", f)
                   for f in ("fa_device.hpp", "fa_fwd16.hpp", "fa_fwd_kernel.hpp", "fa_fwd_short.hpp",
-                            "fa_api.hip")]
+                            "fa_api.hip", "fa_host.hpp")]
 BWD_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_23_amd", "csrc", f)
-                      for f in ("fa_device.hpp", "fa_bwd_kernel.hpp", "fa_bwd.hip")]
+                      for f in ("fa_device.hpp", "fa_bwd_kernel.hpp", "fa_bwd.hip", "fa_host.hpp")]
 FP8_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_23_amd", "csrc", f)
-                      for f in ("fa_device.hpp", "fa_fwd_kernel.hpp", "fa_fwd_fp8.hpp", "fa_fp8.hip")]
+                      for f in ("fa_device.hpp", "fa_fwd_kernel.hpp", "fa_fwd_fp8.hpp", "fa_fp8.hip",
+                                "fa_host.hpp")]
 STD_KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_23_amd", "csrc", f)
                       for f in ("fa_device.hpp", "fa_std_kernel.hpp", "fa_std.hip")]
 STD_KERNELS = ("fa_std_scores_kernel", "fa_std_softmax_kernel", "fa_std_pv_kernel")

@@ -291,25 +291,17 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   p.total = (int)total;
   p.xcd_q = (int)(total / 8);
   p.xcd_r = (int)(total % 8);
-  // Heads per scheduling group (see work_item): the workgroups of a group's
-  // heads are interleaved, heaviest first. Causal launches take as many heads
-  // as fit their K and V in 2 MiB, half of an XCD's 4 MB L2, between 1 and
-  // 8: the resident workgroups of an XCD then stream a working set the L2
-  // holds, and the launch ends on light blocks of several heads instead of
-  // the heavy blocks of one. Measured on causal 16-bit inputs: N = 2048,
-  // d = 64 (512 KB per head, groups of 4) runs 5% faster than with one head
-  // per group; N = 16384, d = 128 (8 MB per head) keeps one head, since
-  // groups of 8 there run 30% slower. Without a mask every block has the
-  // same work and grouping only widens the set of heads in flight (N = 6400,
-  // d = 32 in groups of 2 read 11% more from HBM), so each head is its own
-  // group.
+  // Heads per scheduling group and the per-XCD numbering (see work_item and
+  // fa::causal_order). Without a mask every block has the same work and
+  // grouping only widens the set of heads in flight (N = 6400, d = 32 in
+  // groups of 2 read 11% more from HBM), so each head is its own group.
   if (causal) {
-    const int64_t kv_head_bytes = 2 * Nk * d * 2;
-    int64_t g = ((int64_t)2 << 20) / kv_head_bytes;
-    g = g < 1 ? 1 : (g > 8 ? 8 : g);
-    p.group = (int)(g < B * H ? g : B * H);
+    const fa::CausalOrder co = fa::causal_order(B * H, 2 * Nk * d * 2);
+    p.group = co.group;
+    p.launch_order = co.launch_order;
   } else {
     p.group = 1;
+    p.launch_order = 0;
   }
   p.nkt = (int)key_tiles;
   p.sq = {sq.b, sq.h, (int)sq.n};

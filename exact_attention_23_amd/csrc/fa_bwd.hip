@@ -177,7 +177,16 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
   p.Nq = (int)Nq;
   p.Nk = (int)Nk;
   p.nrec = (int)nrec;
-  p.group = 1;
+  // Causal blocks in the forward's order (fa::causal_order): a dK/dV block
+  // streams its head's Q and dO, a dQ block its head's K and V.
+  if (causal) {
+    const fa::CausalOrder co = fa::causal_order(B * H, 2 * Nq * d * 2);
+    p.group = co.group;
+    p.launch_order = co.launch_order;
+  } else {
+    p.group = 1;
+    p.launch_order = 0;
+  }
   p.c = scale * fa::kLog2e;
   p.scale = scale;
   hipStream_t st = (hipStream_t)stream;

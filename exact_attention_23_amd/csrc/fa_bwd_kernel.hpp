@@ -81,21 +81,22 @@ struct BwdParams {
   int xcd_q;     // workgroups / 8
   int xcd_r;     // workgroups % 8
   int group;     // heads per scheduling group
+  int launch_order;  // nonzero: logical id = workgroup id (no per-XCD ranges)
   float c;       // scale * log2(e)
   float scale;
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Workgroup id -> (head, block), with the same XCD-contiguous remap as the
-// forward. DESC walks the blocks of a head from the last one (the heaviest
+// Workgroup id -> (head, block), with the same XCD-contiguous remap (or launch
+// order) and head groups as the forward. DESC walks the blocks of a head from the last one (the heaviest
 // for causal dQ, whose late query blocks see the most keys); ascending order
 // puts the heaviest causal dK/dV blocks (early keys) first.
 template <bool DESC>
 __device__ __forceinline__ void bwd_work_item(const BwdParams& p, int bid, int& head, int& blk) {
   const int xcd = bid & 7;
   const int slot = bid >> 3;
-  const int L = xcd * p.xcd_q + (xcd < p.xcd_r ? xcd : p.xcd_r) + slot;
+  const int L = p.launch_order ? bid : xcd * p.xcd_q + (xcd < p.xcd_r ? xcd : p.xcd_r) + slot;
   const int per_group = p.group * p.nblk;
   const int grp = L / per_group;
   const int rem = L - grp * per_group;

@@ -84,7 +84,14 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   p.total = (int)total;
   p.xcd_q = fa::xcd_split(total).q;
   p.xcd_r = fa::xcd_split(total).r;
-  p.group = 1;
+  if (causal) {  // the order of the 16-bit forward of the same shape
+    const fa::CausalOrder co = fa::causal_order(B * H, 2 * Nk * d * 2);
+    p.group = co.group;
+    p.launch_order = co.launch_order;
+  } else {
+    p.group = 1;
+    p.launch_order = 0;
+  }
   p.nkt = 0;
   if (qk == 0.0f) {  // every score is 0: zero Q, any positive factor works
     p.c = 1.0f;

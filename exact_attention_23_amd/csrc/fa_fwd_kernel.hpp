@@ -88,6 +88,7 @@ struct Params {
   int xcd_q;      // total / 8
   int xcd_r;      // total % 8
   int group;      // heads per scheduling group
+  int launch_order;  // nonzero: logical id = workgroup id (no per-XCD ranges)
   float c;        // |scale| * log2(e), or 1 when scale == 0
   uint32_t q_and; // applied to each 32-bit word of Q: ~0 normally, 0 when scale == 0
   uint32_t q_xor; // 0x80008000 flips both halves' sign when scale < 0
@@ -120,7 +121,7 @@ template <bool CAUSAL>
 __device__ __forceinline__ void work_item(const Params& p, int bid, int& head, int& qb) {
   const int xcd = bid & 7;
   const int slot = bid >> 3;
-  const int L = xcd * p.xcd_q + (xcd < p.xcd_r ? xcd : p.xcd_r) + slot;
+  const int L = p.launch_order ? bid : xcd * p.xcd_q + (xcd < p.xcd_r ? xcd : p.xcd_r) + slot;
   const int per_group = p.group * p.num_qb;
   const int grp = L / per_group;
   const int rem = L - grp * per_group;
