@@ -128,24 +128,42 @@ int64_t stream_grid(const StreamVariant& sv) {
   return (int64_t)per_cu * fa::device_cus();
 }
 
-// The short-range kernel for one head width: its launch function and the most
-// 64-key tiles it takes.
+// The short-range kernel for one head width and tile count: its launch
+// function and how many of its workgroups a compute unit holds (LDS for
+// NWMAX waves, at most 16 waves).
 template <typename T>
 struct ShortVariant {
   KernelFn fn;
-  int max_tiles;
+  int per_cu;
 };
+template <int D, int NWMAX, int QB, typename T>
+ShortVariant<T> short_of(bool causal) {
+  constexpr int lds = NWMAX * fa::kShortRegion<D, QB> + 3 * NWMAX * 16 * QB * 4;
+  constexpr int by_lds = (160 * 1024) / lds;
+  constexpr int by_waves = 16 / NWMAX;
+  constexpr int per_cu = by_lds < by_waves ? by_lds : by_waves;
+  return {causal ? fa::fa_fwd_short_kernel<D, NWMAX, QB, true, T> : fa::fa_fwd_short_kernel<D, NWMAX, QB, false, T>,
+          per_cu < 1 ? 1 : per_cu};
+}
+template <int D, int QB, typename T>
+ShortVariant<T> make_short_qb(bool causal, int64_t tiles) {
+  if constexpr (D == 128) {
+    return short_of<128, fa::kShortMaxWaves<128>, QB, T>(causal);
+  } else {
+    if (tiles <= 8) return short_of<D, 8, QB, T>(causal);
+    return short_of<D, 16, QB, T>(causal);
+  }
+}
 template <int D, typename T>
-ShortVariant<T> make_short(bool causal) {
-  return {causal ? fa::fa_fwd_short_kernel<D, true, T> : fa::fa_fwd_short_kernel<D, false, T>,
-          fa::kShortMaxWaves<D>};
+ShortVariant<T> make_short(bool causal, int64_t tiles, int qb) {
+  return qb == 1 ? make_short_qb<D, 1, T>(causal, tiles) : make_short_qb<D, 2, T>(causal, tiles);
 }
 template <typename T>
-ShortVariant<T> pick_short(int64_t d, bool causal) {
+ShortVariant<T> pick_short(int64_t d, bool causal, int64_t tiles, int qb) {
   switch (d) {
-    case 32: return make_short<32, T>(causal);
-    case 64: return make_short<64, T>(causal);
-    default: return make_short<128, T>(causal);
+    case 32: return make_short<32, T>(causal, tiles, qb);
+    case 64: return make_short<64, T>(causal, tiles, qb);
+    default: return make_short<128, T>(causal, tiles, qb);
   }
 }
 
@@ -270,12 +288,25 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   const int short_max = d == 128 ? fa::kShortMaxWaves<128> : fa::kShortMaxWaves<64>;
   const bool short_fits = key_tiles <= short_max;
   if (path == FA_PATH_SHORT && !short_fits) return FA_ERR_PATH;
-  const int64_t short_total = B * H * ((Nq + 31) / 32);
-  if (short_total >= lim) return FA_ERR_SHAPE;
-  // Latency-bound sizes: the short path's workgroups (one per 32 rows, at
-  // most one per compute unit for its LDS) all run at once.
-  const bool use_short =
-      path == FA_PATH_SHORT || (path == FA_PATH_AUTO && short_fits && short_total <= fa::device_cus());
+  // Latency-bound sizes take the short path when its workgroups all run at
+  // once: one 16-row block per workgroup when those fit one per compute
+  // unit, else two blocks per workgroup (one per unit, or as many as their
+  // LDS lets a unit hold). An explicit short path takes the same choice and
+  // runs in rounds when needed.
+  const int64_t short_t1 = B * H * ((Nq + 15) / 16), short_t2 = B * H * ((Nq + 31) / 32);
+  int short_qb = 0;  // 0: the tiled path
+  if (short_fits && path != FA_PATH_TILED) {
+    const int64_t cus = fa::device_cus();
+    const int per_cu2 = dtype == FA_DTYPE_FP16 ? pick_short<_Float16>(d, causal != 0, key_tiles, 2).per_cu
+                                               : pick_short<__bf16>(d, causal != 0, key_tiles, 2).per_cu;
+    if (short_t1 <= cus)
+      short_qb = 1;
+    else if (path == FA_PATH_SHORT || short_t2 <= (int64_t)per_cu2 * cus)
+      short_qb = 2;
+  }
+  const bool use_short = short_qb != 0;
+  const int64_t short_total = short_qb == 1 ? short_t1 : short_t2;
+  if (use_short && short_total >= lim) return FA_ERR_SHAPE;
 
   fa::Params p;
   p.q = q;
@@ -351,9 +382,9 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   void* args[] = {&p};
   hipError_t e;
   if (use_short) {
-    const KernelFn fn = dtype == FA_DTYPE_FP16 ? pick_short<_Float16>(d, causal != 0).fn
-                                               : pick_short<__bf16>(d, causal != 0).fn;
-    p.num_qb = (int)((Nq + 31) / 32);
+    const KernelFn fn = dtype == FA_DTYPE_FP16 ? pick_short<_Float16>(d, causal != 0, key_tiles, short_qb).fn
+                                               : pick_short<__bf16>(d, causal != 0, key_tiles, short_qb).fn;
+    p.num_qb = (int)((Nq + 16 * short_qb - 1) / (16 * short_qb));
     p.total = (int)short_total;
     p.xcd_q = (int)(short_total / 8);
     p.xcd_r = (int)(short_total % 8);
