@@ -294,6 +294,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   // LDS lets a unit hold). An explicit short path takes the same choice and
   // runs in rounds when needed.
   const int64_t short_t1 = B * H * ((Nq + 15) / 16), short_t2 = B * H * ((Nq + 31) / 32);
+  if (path == FA_PATH_SHORT && short_t2 >= lim) return FA_ERR_SHAPE;
   int short_qb = 0;  // 0: the tiled path
   if (short_fits && path != FA_PATH_TILED) {
     const int64_t cus = fa::device_cus();
@@ -304,9 +305,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
     else if (path == FA_PATH_SHORT || short_t2 <= (int64_t)per_cu2 * cus)
       short_qb = 2;
   }
-  const bool use_short = short_qb != 0;
+  const bool use_short = short_qb != 0;  // its workgroup count is below lim (checked or bounded by the CUs)
   const int64_t short_total = short_qb == 1 ? short_t1 : short_t2;
-  if (use_short && short_total >= lim) return FA_ERR_SHAPE;
 
   fa::Params p;
   p.q = q;
