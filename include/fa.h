@@ -103,16 +103,18 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *                  keys tile after tile through LDS, updating the running
  *                  maximum, sum and output as in the online softmax of the
  *                  kwkr.cn YOLO11 FlashAttention-2 article, section 1.2.
- *   FA_PATH_SHORT  for short key ranges: one workgroup per 32 query rows
- *                  takes every 64-key tile at once, one wave per tile, and
- *                  combines the per-tile maxima, sums and outputs exactly
- *                  (the same rescaling, applied across tiles in parallel).
- *                  Requires ceil(Nk / 64) <= 16 for d = 32 and 64, <= 9 for
- *                  d = 128 (Nk <= 1024 or 576).
- *   FA_PATH_AUTO   FA_PATH_SHORT when it applies and its workgroups
- *                  (B*H*ceil(Nq/32)) are no more than the GPU's compute units,
- *                  so they all run at once (latency-bound sizes);
- *                  FA_PATH_TILED otherwise. */
+ *   FA_PATH_SHORT  for short key ranges: one workgroup per 16 query rows
+ *                  (B*H*ceil(Nq/16) workgroups when those are no more than
+ *                  the GPU's compute units, else one per 32 rows) takes every
+ *                  64-key tile at once, one wave per tile, and combines the
+ *                  per-tile maxima, sums and outputs exactly (the same
+ *                  rescaling, applied across tiles in parallel). Requires
+ *                  ceil(Nk / 64) <= 16 for d = 32 and 64, <= 9 for d = 128
+ *                  (Nk <= 1024 or 576).
+ *   FA_PATH_AUTO   FA_PATH_SHORT when it applies and its workgroups all run
+ *                  at once (16-row workgroups at most one per compute unit,
+ *                  or 32-row ones as many as the units' LDS holds:
+ *                  latency-bound sizes); FA_PATH_TILED otherwise. */
 enum fa_path { FA_PATH_AUTO = 0, FA_PATH_TILED = 1, FA_PATH_SHORT = 2 };
 
 /*
