@@ -22,15 +22,29 @@ from tests.test_random_shapes import _cases as shape_cases
 from workloads import WORKLOADS, make_inputs
 
 
+def _short_per_cu(d, tiles):
+    """Two-block short-range workgroups a compute unit holds (LDS for NWMAX
+    waves, at most 16 waves), as the library counts them."""
+    nwmax = 9 if d == 128 else (8 if tiles <= 8 else 16)
+    region = max(64 * d * 2, 32 * (d + 4) * 4)
+    lds = nwmax * region + 3 * nwmax * 32 * 4
+    return max(1, min((160 * 1024) // lds, 16 // nwmax))
+
+
 def _kernel_of(c):
     """The forward kernel a random case runs: its explicit path, or the
     automatic choice (the short-range kernel when its key range fits and its
-    workgroups, one per 32 rows, fit the 256 compute units at once)."""
+    workgroups all run at once: one per 16 rows at most one per compute unit
+    of 256, else one per 32 rows as many as the units hold)."""
     path = c.get("path", "auto")
     if path != "auto":
         return path
-    fits = (c["Nk"] + 63) // 64 <= (9 if c["d"] == 128 else 16)
-    return "short" if fits and c["B"] * c["H"] * ((c["Nq"] + 31) // 32) <= 256 else "tiled"
+    tiles = (c["Nk"] + 63) // 64
+    fits = tiles <= (9 if c["d"] == 128 else 16)
+    heads = c["B"] * c["H"]
+    t1, t2 = heads * ((c["Nq"] + 15) // 16), heads * ((c["Nq"] + 31) // 32)
+    short = fits and (t1 <= 256 or t2 <= _short_per_cu(c["d"], tiles) * 256)
+    return "short" if short else "tiled"
 
 
 def _errors(c, norm, kernel):
